@@ -1,0 +1,200 @@
+/*
+ * mla_decode.h — C ABI of the MI355X (gfx950) MLA paged-KV decode library.
+ *
+ * Operation (what every entry point computes): Multi-head Latent Attention
+ * decode over a paged latent KV cache.
+ *   - A cache row is 576 elements: a 512-wide latent, which is also the value
+ *     vector V, followed by a 64-wide RoPE part (tokenspeed-mla package page,
+ *     "Quickstart": kv_lora_rank = 512, qk_rope_head_dim = 64).
+ *   - Sequence b's key j is row (j % page_size) of page
+ *     block_table[b * max_pages + j / page_size] (TokenSpeed MLA article,
+ *     section 6: kv_cache [num_pages, page_size, D_total] with block_tables).
+ *   - Queries are [batch, q_len, num_heads, 576]; token t of q_len attends to
+ *     keys j < seq_lens[b] - q_len + t + 1 (causal across the new tokens, the
+ *     sequence length counting them; a row with no visible key gets O = 0 and
+ *     LSE = -inf).
+ *   - score = softmax_scale * (q_scale * q) . (kv_scale * k) over all 576
+ *     dims; O = softmax(score) @ V (first 512 dims), written as bf16;
+ *     LSE = natural log of sum exp(score), fp32.
+ *   - Work is split along the KV sequence into partial (O, LSE) pieces that a
+ *     second kernel merges by LSE weighting (article, section 2); query
+ *     tokens are folded into the head dimension, F = the largest divisor of
+ *     q_len with num_heads * F <= 128 (article, section 3).
+ *
+ * Conventions for every entry point:
+ *   - Return 0 (MLA_OK) or a negative mla_status; mla_last_error() then holds
+ *     a message for the calling thread.  Arguments are validated on the host
+ *     before anything is enqueued: a failed call enqueues nothing.
+ *   - Pointers documented "device" are HIP device pointers; the library never
+ *     reads device memory on the host, never allocates or frees memory and
+ *     never synchronises: calls enqueue on `stream` (a hipStream_t, NULL for
+ *     the default stream) and return.  Faults inside kernels surface at the
+ *     caller's next synchronisation.  No memset is enqueued, so calls may be
+ *     captured into a HIP graph.
+ *   - The caller owns every buffer.  Calls that share a workspace on streams
+ *     that run concurrently race on it.
+ *   - Thread-safe: the per-shape plan cache is guarded by a mutex.
+ */
+#ifndef MLA_DECODE_H_
+#define MLA_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_VERSION 100 /* 1.0.0 */
+
+#define MLA_D_QK 576 /* latent 512 + rope 64 */
+#define MLA_D_V 512
+#define MLA_KV_LORA_RANK 512
+#define MLA_QK_ROPE_HEAD_DIM 64
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,        /* a required pointer is NULL */
+  MLA_ERR_DTYPE = -2,       /* dtype code not accepted */
+  MLA_ERR_SHAPE = -3,       /* a size is out of range or inconsistent */
+  MLA_ERR_ALIGN = -4,       /* a device pointer is not aligned as required */
+  MLA_ERR_WORKSPACE = -5,   /* workspace NULL, too small, misaligned, or planned for another shape */
+  MLA_ERR_UNSUPPORTED = -6, /* valid but not implemented (e.g. fp16) */
+  MLA_ERR_HIP = -7,         /* a HIP runtime call failed (message names it) */
+  MLA_ERR_DEVICE = -8       /* no usable HIP device */
+} mla_status;
+
+typedef enum mla_dtype {
+  MLA_DTYPE_BF16 = 1,     /* bfloat16, stored as 16-bit patterns */
+  MLA_DTYPE_FP8_E4M3 = 2, /* OCP FP8 E4M3 (e4m3fn): bias 7, no inf, S.1111.111 = NaN, max 448 */
+  MLA_DTYPE_FP16 = 3      /* reserved: returns MLA_ERR_UNSUPPORTED */
+} mla_dtype;
+
+/* Sizes of one decode call.  All fields are element counts. */
+typedef struct mla_shape {
+  int32_t batch;       /* B >= 0 sequences */
+  int32_t q_len;       /* new query tokens per sequence, >= 1 */
+  int32_t num_heads;   /* H >= 1 query heads sharing the one latent KV head */
+  int32_t num_pages;   /* pages in kv_cache, >= 1 */
+  int32_t page_size;   /* rows per page: a power of two, 16 <= page_size <= 65536 */
+  int32_t max_pages;   /* entries per block_table row (its row stride), >= 1 */
+  int32_t max_seq_len; /* the length the workspace was planned for (upper bound of seq_lens);
+                          0 <= max_seq_len <= max_pages * page_size */
+  int32_t dtype;       /* mla_dtype of q and kv_cache (both the same) */
+} mla_shape;
+
+/*
+ * Plan a decode shape: the number of KV splits and the workspace size.
+ *
+ * The split count and workspace are derived from (batch, q_len, num_heads,
+ * max_seq_len) and the current device's compute-unit count and cached per
+ * shape, so callers never tune them (article, section 2: split_kv and the
+ * workspace size are derived at run time from batch size, q_len and
+ * max_seq_len, and cached).  num_splits is the number of KV slices the
+ * batch's total work is cut into; workspace_bytes is what mla_decode needs
+ * for that shape (0 when no merge is needed).
+ *
+ * Inputs are host integers; outputs are host pointers (must be non-NULL).
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE (batch < 0, q_len < 1, num_heads < 1,
+ * max_seq_len < 0), MLA_ERR_DEVICE / MLA_ERR_HIP when the device cannot be
+ * queried.
+ */
+int mla_get_split_kv_and_workspace(int32_t batch, int32_t q_len, int32_t num_heads, int32_t max_seq_len,
+                                   int32_t* num_splits, size_t* workspace_bytes);
+
+/*
+ * MLA decode (the operation described at the top of this file).
+ *
+ *   shape       host pointer to the call's sizes.
+ *   q           device, [batch, q_len, num_heads, 576] of shape->dtype, contiguous, 16-byte aligned.
+ *   kv_cache    device, [num_pages, page_size, 576] of shape->dtype, contiguous, 16-byte aligned.
+ *   block_table device int32, [batch, max_pages] row-major.  The first
+ *               ceil(seq_lens[b] / page_size) entries of row b must be page
+ *               indices in [0, num_pages); later entries are never read.
+ *               Out-of-range entries are clamped into range (no out-of-bounds
+ *               access; results for that sequence are then unspecified).
+ *   seq_lens    device int32 [batch], each >= 0 (keys in the cache for that
+ *               sequence, including the q_len new tokens).  Values above
+ *               max_seq_len are still computed correctly (less balanced).
+ *   softmax_scale, q_scale, kv_scale
+ *               host floats; dequantised value = stored value * scale (pass
+ *               1.0 for bf16 data).
+ *   out         device bf16 [batch, q_len, num_heads, 512], contiguous, 16-byte aligned.
+ *   lse         device fp32 [batch, q_len, num_heads] or NULL to skip.
+ *   workspace   device scratch of workspace_bytes bytes, 256-byte aligned, at
+ *               least the size mla_get_split_kv_and_workspace returns for
+ *               (batch, q_len, num_heads, max_seq_len); may be NULL when that
+ *               size is 0.  Its contents need no initialisation.
+ *   stream      hipStream_t or NULL.
+ *
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_DTYPE, MLA_ERR_UNSUPPORTED
+ * (fp16), MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_DEVICE, MLA_ERR_HIP
+ * (kernel launch failed).  batch == 0 returns MLA_OK and enqueues nothing.
+ */
+int mla_decode(const mla_shape* shape, const void* q, const void* kv_cache, const int32_t* block_table,
+               const int32_t* seq_lens, float softmax_scale, float q_scale, float kv_scale, void* out, float* lse,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Knobs of mla_decode_ex, for tests and tuning.  Zero-initialise, then set. */
+typedef struct mla_options {
+  int32_t num_splits;   /* > 0: use this many KV slices instead of the planned count */
+  int32_t no_fold;      /* != 0: do not fold query tokens into heads (F = 1) */
+  int32_t partial_bf16; /* != 0: keep the split partial outputs as bf16 instead of fp32 */
+  int32_t reserved[5];
+  void* split_event;    /* hipEvent_t or NULL: recorded on `stream` after the split-KV kernel
+                           and before the merge kernel, so callers can time each kernel */
+} mla_options;
+
+/*
+ * mla_decode with explicit options.  The workspace must be sized with
+ * mla_workspace_bytes_ex for the same options.  Results equal mla_decode's
+ * up to floating-point summation order (the fold factor only re-indexes rows;
+ * the split count only changes where the LSE merge happens).
+ */
+int mla_decode_ex(const mla_shape* shape, const void* q, const void* kv_cache, const int32_t* block_table,
+                  const int32_t* seq_lens, float softmax_scale, float q_scale, float kv_scale, void* out,
+                  float* lse, void* workspace, size_t workspace_bytes, void* stream, const mla_options* options);
+
+/* Workspace size and split count for mla_decode_ex with `options` (NULL = defaults). */
+int mla_workspace_bytes_ex(int32_t batch, int32_t q_len, int32_t num_heads, int32_t max_seq_len,
+                           const mla_options* options, int32_t* num_splits, size_t* workspace_bytes);
+
+/*
+ * Host-only planning for an explicit compute-unit count (no device query), so
+ * the split heuristic can be checked without a GPU.  fold_factor receives F.
+ */
+int mla_plan_for_cus(int32_t batch, int32_t q_len, int32_t num_heads, int32_t max_seq_len, int32_t num_cus,
+                     const mla_options* options, int32_t* num_splits, int32_t* fold_factor,
+                     size_t* workspace_bytes);
+
+/*
+ * Fused K/V pack + FP8 quantise: the step that writes decode's cache rows.
+ * Row t of the output is e4m3(latent[t, 0:512] / kv_scale) ||
+ * e4m3(rope[t, 0:64] / kv_scale), round-to-nearest-even with saturation to
+ * +-448 (NaN stays NaN).  It replaces a separate concatenation and cast
+ * (tokenspeed-mla package page, "What it is": the fused K/V packing and FP8
+ * quantisation kernel; TokenSpeed MLA article, section 1, kernel table).
+ *
+ *   latent        device bf16 [num_tokens, 512], row stride latent_stride elements (>= 512), 16-byte aligned rows.
+ *   rope          device bf16 [num_tokens, 64],  row stride rope_stride elements (>= 64), 16-byte aligned rows.
+ *   slot_mapping  device int64 [num_tokens] or NULL.  NULL: token t goes to
+ *                 row t of out.  Otherwise to row slot_mapping[t] of out;
+ *                 negative slots are skipped; slots >= out_rows are skipped.
+ *   out           device uint8 [out_rows, 576] (e.g. a paged cache viewed as rows), 16-byte aligned.
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_ALIGN, MLA_ERR_HIP.
+ */
+int mla_kv_pack_quantize_fp8(const void* latent, int64_t latent_stride, const void* rope, int64_t rope_stride,
+                             const int64_t* slot_mapping, int32_t num_tokens, float kv_scale, void* out,
+                             int64_t out_rows, void* stream);
+
+/* Message for the calling thread's last non-zero return ("" if none). */
+const char* mla_last_error(void);
+
+/* MLA_VERSION of the built library. */
+int mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H_ */

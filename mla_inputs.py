@@ -11,7 +11,9 @@ order of draws:
   2. a permutation of the page pool (block_table rows take consecutive pages
      of it; unreferenced pool pages are spares);
   3. q ~ N(0, 1), shape [B, q_len, H, 576];
-  4. the page pool ~ N(0, 1), shape [num_pages, page_size, 576].
+  4. the page pool ~ N(0, 1), shape [num_pages, page_size, 576], drawn in
+     chunks of 256 pages in page order (for FP8 the stream is replayed: a
+     first pass finds the pool's amax, a second quantises).
 bf16 inputs are cast round-to-nearest-even; FP8 inputs use one per-tensor
 scale amax/448 each for q and for the cache, clamp to +-448 and cast to OCP
 E4M3 (e4m3fn), so dequantised value = code * scale.  Spare pages are filled
@@ -100,6 +102,36 @@ def _quantize(x: np.ndarray, dtype: int):
     return _cast_e4m3(x, scale), scale
 
 
+POOL_CHUNK_PAGES = 256
+
+
+def _draw_pool(rng, num_pages, page_size, dtype):
+    """N(0,1) pool drawn chunk by chunk into a preallocated output (no large temporaries)."""
+    shape = (num_pages, page_size, D_QK)
+    buf = np.empty((POOL_CHUNK_PAGES, page_size, D_QK), dtype=np.float32)
+    if dtype == BF16:
+        out = np.empty(shape, dtype=np.uint16)
+        for p0 in range(0, num_pages, POOL_CHUNK_PAGES):
+            n = min(POOL_CHUNK_PAGES, num_pages - p0)
+            rng.standard_normal(out=buf[:n], dtype=np.float32)
+            out[p0:p0 + n] = _cast_bf16(buf[:n])
+        return out, 1.0
+    state = rng.bit_generator.state
+    amax = 0.0
+    for p0 in range(0, num_pages, POOL_CHUNK_PAGES):
+        n = min(POOL_CHUNK_PAGES, num_pages - p0)
+        rng.standard_normal(out=buf[:n], dtype=np.float32)
+        amax = max(amax, float(buf[:n].max()), float(-buf[:n].min()))
+    scale = amax / 448.0 if amax > 0 else 1.0
+    rng.bit_generator.state = state
+    out = np.empty(shape, dtype=np.uint8)
+    for p0 in range(0, num_pages, POOL_CHUNK_PAGES):
+        n = min(POOL_CHUNK_PAGES, num_pages - p0)
+        rng.standard_normal(out=buf[:n], dtype=np.float32)
+        out[p0:p0 + n] = _cast_e4m3(buf[:n], scale)
+    return out, scale
+
+
 def _draw_lens(rng, B, spec):
     kind = spec[0]
     if kind == "fixed":
@@ -143,11 +175,9 @@ def make_inputs(B, q_len, H, dtype, lens, *, page_size=64, seed=0, spare_pages=8
     if pool_pages is not None and B == 1:
         block_table[0, :] = perm[:max_pages]
     q32 = rng.standard_normal((B, q_len, H, D_QK), dtype=np.float32)
-    kv32 = rng.standard_normal((num_pages, page_size, D_QK), dtype=np.float32)
     q, q_scale = _quantize(q32, dtype)
     del q32
-    kv, kv_scale = _quantize(kv32, dtype)
-    del kv32
+    kv, kv_scale = _draw_pool(rng, num_pages, page_size, dtype)
     nan_code = NAN_BF16 if dtype == BF16 else NAN_E4M3
     used = np.zeros(num_pages, dtype=bool)
     for b in range(B):

@@ -1,0 +1,222 @@
+"""Python binding of the MI355X MLA paged-KV decode library (libmla_decode.so).
+
+Argument marshalling only: every step of the decode runs in the library's
+HIP kernels.  PyTorch provides device memory and the current stream.  The
+library must be built (``python -m mla_paged_kv_decode_amd.build``); without
+it every call raises -- there is no fallback implementation.
+
+Entry points mirror include/mla_decode.h:
+  plan(B, q_len, H, max_seq_len)            -> (num_splits, workspace_bytes)
+  decode(q, kv_cache, block_table, seq_lens, softmax_scale, ...) -> (out, lse)
+  kv_pack_quantize_fp8(latent, rope, kv_scale, ...) -> uint8 rows [T, 576]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla_decode.so")
+
+D_QK = 576
+D_V = 512
+DTYPE_BF16 = 1
+DTYPE_FP8_E4M3 = 2
+DTYPE_FP16 = 3
+
+STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_DTYPE", -3: "MLA_ERR_SHAPE", -4: "MLA_ERR_ALIGN",
+          -5: "MLA_ERR_WORKSPACE", -6: "MLA_ERR_UNSUPPORTED", -7: "MLA_ERR_HIP", -8: "MLA_ERR_DEVICE"}
+
+# every symbol include/mla_decode.h declares
+EXPORTS = ["mla_get_split_kv_and_workspace", "mla_decode", "mla_decode_ex", "mla_workspace_bytes_ex",
+           "mla_plan_for_cus", "mla_kv_pack_quantize_fp8", "mla_last_error", "mla_version"]
+
+
+class MlaError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{STATUS.get(code, code)}: {message}")
+        self.code = code
+
+
+class MlaShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("q_len", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class MlaOptions(ctypes.Structure):
+    _fields_ = [("num_splits", ctypes.c_int32), ("no_fold", ctypes.c_int32), ("partial_bf16", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 5), ("split_event", ctypes.c_void_p)]
+
+
+def options(num_splits: int = 0, no_fold: bool = False, partial_bf16: bool = False, split_event=None) -> MlaOptions:
+    """mla_options; split_event is a raw hipEvent_t (e.g. torch.cuda.Event().cuda_event after one record)."""
+    o = MlaOptions()
+    o.num_splits = int(num_splits)
+    o.no_fold = int(bool(no_fold))
+    o.partial_bf16 = int(bool(partial_bf16))
+    o.split_event = split_event
+    return o
+
+
+_lib = None
+
+
+def lib():
+    """Load libmla_decode.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m mla_paged_kv_decode_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, p, sz = ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+    L.mla_get_split_kv_and_workspace.argtypes = [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(sz)]
+    L.mla_workspace_bytes_ex.argtypes = [i32, i32, i32, i32, ctypes.POINTER(MlaOptions), ctypes.POINTER(i32),
+                                         ctypes.POINTER(sz)]
+    L.mla_plan_for_cus.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(MlaOptions), ctypes.POINTER(i32),
+                                   ctypes.POINTER(i32), ctypes.POINTER(sz)]
+    dec = [ctypes.POINTER(MlaShape), p, p, p, p, ctypes.c_float, ctypes.c_float, ctypes.c_float, p, p, p, sz, p]
+    L.mla_decode.argtypes = dec
+    L.mla_decode_ex.argtypes = dec + [ctypes.POINTER(MlaOptions)]
+    L.mla_kv_pack_quantize_fp8.argtypes = [p, ctypes.c_int64, p, ctypes.c_int64, p, i32, ctypes.c_float, p,
+                                           ctypes.c_int64, p]
+    L.mla_last_error.restype = ctypes.c_char_p
+    L.mla_last_error.argtypes = []
+    L.mla_version.restype = ctypes.c_int
+    for f in ("mla_get_split_kv_and_workspace", "mla_workspace_bytes_ex", "mla_plan_for_cus", "mla_decode",
+              "mla_decode_ex", "mla_kv_pack_quantize_fp8"):
+        getattr(L, f).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise MlaError(rc, lib().mla_last_error().decode())
+
+
+def plan(batch: int, q_len: int, num_heads: int, max_seq_len: int, opts: MlaOptions | None = None):
+    """(num_splits, workspace_bytes) for a shape on the current device."""
+    ns, ws = ctypes.c_int32(), ctypes.c_size_t()
+    if opts is None:
+        _check(lib().mla_get_split_kv_and_workspace(batch, q_len, num_heads, max_seq_len, ctypes.byref(ns),
+                                                    ctypes.byref(ws)))
+    else:
+        _check(lib().mla_workspace_bytes_ex(batch, q_len, num_heads, max_seq_len, ctypes.byref(opts),
+                                            ctypes.byref(ns), ctypes.byref(ws)))
+    return ns.value, ws.value
+
+
+def plan_for_cus(batch: int, q_len: int, num_heads: int, max_seq_len: int, num_cus: int,
+                 opts: MlaOptions | None = None):
+    """Host-only plan for an explicit compute-unit count: (num_splits, fold_factor, workspace_bytes)."""
+    ns, fold, ws = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_size_t()
+    _check(lib().mla_plan_for_cus(batch, q_len, num_heads, max_seq_len, num_cus,
+                                  ctypes.byref(opts) if opts is not None else None, ctypes.byref(ns),
+                                  ctypes.byref(fold), ctypes.byref(ws)))
+    return ns.value, fold.value, ws.value
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return DTYPE_FP8_E4M3
+    if t.dtype == torch.float16:
+        return DTYPE_FP16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def make_shape(q, kv_cache, block_table, max_seq_len: int) -> MlaShape:
+    s = MlaShape()
+    s.batch, s.q_len, s.num_heads = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    s.num_pages, s.page_size = int(kv_cache.shape[0]), int(kv_cache.shape[1])
+    s.max_pages = int(block_table.shape[1])
+    s.max_seq_len = int(max_seq_len)
+    s.dtype = _dtype_code(q)
+    return s
+
+
+def _check_layout(q, kv_cache, block_table, seq_lens):
+    torch = _torch()
+    if q.dim() != 4 or q.shape[3] != D_QK or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, q_len, H, 576] tensor")
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != D_QK or not kv_cache.is_contiguous():
+        raise ValueError("kv_cache must be a contiguous [num_pages, page_size, 576] tensor")
+    if _dtype_code(q) != _dtype_code(kv_cache):
+        raise TypeError("q and kv_cache must have the same dtype")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be int32 [B, max_pages] with unit column stride")
+    if block_table.stride(0) != block_table.shape[1]:
+        raise ValueError("block_table rows must be packed (row stride = max_pages)")
+    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
+
+
+def decode(q, kv_cache, block_table, seq_lens, softmax_scale: float, q_scale: float = 1.0, kv_scale: float = 1.0,
+           *, max_seq_len: int | None = None, out=None, lse=None, return_lse: bool = True, workspace=None,
+           opts: MlaOptions | None = None, stream=None):
+    """MLA decode through the C ABI.  Tensors live on the current HIP device.
+
+    q: [B, q_len, H, 576] bfloat16 or float8_e4m3fn; kv_cache: [num_pages,
+    page_size, 576] of the same dtype; block_table: int32 [B, max_pages];
+    seq_lens: int32 [B].  Returns (out bf16 [B, q_len, H, 512], lse fp32
+    [B, q_len, H] or None).  max_seq_len defaults to max(seq_lens), which
+    reads seq_lens back to the host (pass it to avoid that synchronisation).
+    """
+    torch = _torch()
+    _check_layout(q, kv_cache, block_table, seq_lens)
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0
+    shape = make_shape(q, kv_cache, block_table, max_seq_len)
+    B, q_len, H = shape.batch, shape.q_len, shape.num_heads
+    if out is None:
+        out = torch.empty((B, q_len, H, D_V), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, q_len, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        _, ws_bytes = plan(B, q_len, H, max_seq_len, opts)
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    args = (ctypes.byref(shape), q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+            float(softmax_scale), float(q_scale), float(kv_scale), out.data_ptr(),
+            lse.data_ptr() if lse is not None else None, workspace.data_ptr(), workspace.numel(), stream)
+    if opts is None:
+        _check(lib().mla_decode(*args))
+    else:
+        _check(lib().mla_decode_ex(*args, ctypes.byref(opts)))
+    return out, lse
+
+
+def kv_pack_quantize_fp8(latent, rope, kv_scale: float, *, slot_mapping=None, out=None, stream=None):
+    """latent [T, 512] bf16 || rope [T, 64] bf16 -> E4M3 rows (uint8 [T, 576] or scattered into `out`)."""
+    torch = _torch()
+    if latent.dtype != torch.bfloat16 or rope.dtype != torch.bfloat16:
+        raise TypeError("latent and rope must be bfloat16")
+    if latent.dim() != 2 or latent.shape[1] != D_V or latent.stride(1) != 1:
+        raise ValueError("latent must be [T, 512] with unit column stride")
+    if rope.dim() != 2 or rope.shape[1] != D_QK - D_V or rope.stride(1) != 1 or rope.shape[0] != latent.shape[0]:
+        raise ValueError("rope must be [T, 64] with unit column stride")
+    T = latent.shape[0]
+    if out is None:
+        if slot_mapping is not None:
+            raise ValueError("pass `out` when scattering through slot_mapping")
+        out = torch.empty((T, D_QK), dtype=torch.uint8, device=latent.device)
+    rows = out.numel() // D_QK
+    if slot_mapping is not None and (slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous()):
+        raise ValueError("slot_mapping must be a contiguous int64 tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(latent.device).cuda_stream
+    _check(lib().mla_kv_pack_quantize_fp8(latent.data_ptr(), latent.stride(0), rope.data_ptr(), rope.stride(0),
+                                          slot_mapping.data_ptr() if slot_mapping is not None else None, T,
+                                          float(kv_scale), out.data_ptr(), rows, stream))
+    return out

@@ -1,0 +1,79 @@
+"""Build libmla_decode.so (gfx950 only) in-tree with hipcc.
+
+The library holds the host runtime (csrc/mla_api.cpp) and the HIP kernels
+(csrc/mla_kernels.hip).  The compiler's kernel-resource remarks are parsed
+into a per-kernel report (VGPRs, AGPRs, scratch, LDS, spills) printed after
+the build and kept next to the library as kernel_resources.txt.
+"""
+from __future__ import annotations
+
+import os
+import re
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libmla_decode.so")
+SOURCES = [os.path.join(HERE, "csrc", "mla_kernels.hip"), os.path.join(HERE, "csrc", "mla_api.cpp")]
+ARCH = "gfx950"
+
+FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-I", os.path.join(ROOT, "include"),
+    # keep hipcc from forming packed fp32 instructions (v_pk_*_f32)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-inline-asm",
+    "-Rpass-analysis=kernel-resource-usage",
+]
+
+
+def _hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the library)")
+
+
+def parse_resources(text: str) -> dict:
+    kernels, cur = {}, None
+    for line in text.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = kernels.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z][A-Za-z /\[\]]*?):\s+(\d+)", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = int(m.group(2))
+    return kernels
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = [_hipcc(), *FLAGS, *SOURCES, "-o", tmp]
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if proc.returncode != 0:
+        sys.stderr.write(proc.stdout)
+        raise RuntimeError(f"hipcc failed ({proc.returncode})")
+    os.replace(tmp, LIB)
+    res = parse_resources(proc.stdout)
+    lines = []
+    for name, r in sorted(res.items()):
+        lines.append(
+            f"{name}: VGPRs={r.get('VGPRs')} AGPRs={r.get('AGPRs')} scratch={r.get('ScratchSize [bytes/lane]')} "
+            f"LDS={r.get('LDS Size [bytes/block]')} vgpr_spill={r.get('VGPRs Spill')} sgpr_spill={r.get('SGPRs Spill')} "
+            f"occupancy={r.get('Occupancy [waves/SIMD]')}")
+    with open(os.path.join(HERE, "kernel_resources.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    if verbose:
+        print("\n".join(lines))
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,65 @@
+// Internal interfaces between the host runtime (mla_api.cpp) and the gfx950
+// kernels (mla_kernels.hip).  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kDqk = 576;
+constexpr int kDv = 512;
+constexpr int kTileM = 128;     // folded query rows per workgroup (4 waves x 32 rows)
+constexpr int kUnitKeys = 64;   // keys per work unit of the balanced KV partition
+constexpr int kStages = 4;      // LDS ring of KV tiles
+constexpr int kStageBytes = 36864;  // 64 fp8 rows or 32 bf16 rows of 576 elements
+constexpr int kThreads = 256;
+
+enum KernelDtype { kBf16 = 1, kFp8 = 2 };
+
+// Everything the split-KV partial kernel needs.  Passed by value.
+struct PartialParams {
+  const uint8_t* q;          // [B, q_len, H, 576] elements
+  const uint8_t* kv;         // [num_pages, page_size, 576] elements
+  const int32_t* block_table;  // [B, max_pages]
+  const int32_t* seq_lens;   // [B]
+  uint16_t* out;             // bf16 [B, q_len, H, 512]
+  float* lse;                // [B, q_len, H] or nullptr
+  void* part_o;              // [G + B][q_len * H][512] fp32 or bf16
+  float* part_lse;           // [G + B][q_len * H]
+  int32_t* meta;             // [B][2]: first and last KV slice touching sequence b; then int64 T
+  int32_t B, q_len, H, F, H_eff, q_len_eff, m_tiles, U, G;
+  int32_t xcd_map;           // 1: the U workgroups of a slice are placed on one XCD
+  int32_t page_size, page_shift, max_pages, num_pages;
+  float s_scale_log2;        // softmax_scale * q_scale * kv_scale * log2(e)
+  float v_scale;             // kv_scale (V dequantisation)
+  int32_t part_bf16;
+};
+
+struct CombineParams {
+  const void* part_o;
+  const float* part_lse;
+  const int32_t* meta;
+  uint16_t* out;
+  float* lse;
+  int32_t B, rows_per_b, G;
+  int32_t part_bf16;
+};
+
+struct PackParams {
+  const uint16_t* latent;
+  const uint16_t* rope;
+  const int64_t* slot_mapping;
+  uint8_t* out;
+  int64_t latent_stride, rope_stride, out_rows;
+  int32_t num_tokens;
+  float scale;  // kv_scale: stored code = e4m3(x / scale)
+};
+
+// Launchers (defined in mla_kernels.hip).  Return the launch's hipError_t.
+hipError_t launch_partial(const PartialParams& p, int dtype, bool fast_pages, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+hipError_t launch_pack_fp8(const PackParams& p, hipStream_t stream);
+
+}  // namespace mla

@@ -79,12 +79,14 @@ static void decode_row(const void* base, int dtype, size_t elem_index, int n, do
  * lse: [H].  Returns 0, or -1 if a block_table entry is out of range. */
 static int attend_range(const void* kv, int dtype, const int32_t* bt_row, int num_pages, int page_size,
                         int j0, int j1, int H, const double* qv, double softmax_scale, double kv_scale,
-                        double* scores, double* row, double* o, double* lse) {
+                        double* scores, double* row, double* o, double* lse, double* absv) {
   int n = j1 - j0;
   if (n <= 0) {
     for (int h = 0; h < H; ++h) {
       lse[h] = -INFINITY;
       for (int d = 0; d < ORC_D_V; ++d) o[(size_t)h * ORC_D_V + d] = 0.0;
+      if (absv)
+        for (int d = 0; d < ORC_D_V; ++d) absv[(size_t)h * ORC_D_V + d] = 0.0;
     }
     return 0;
   }
@@ -109,6 +111,8 @@ static int attend_range(const void* kv, int dtype, const int32_t* bt_row, int nu
     lse[h] = mx + log(l);
     for (int k = 0; k < n; ++k) scores[(size_t)h * n + k] = exp(scores[(size_t)h * n + k] - mx) / l;
     for (int d = 0; d < ORC_D_V; ++d) o[(size_t)h * ORC_D_V + d] = 0.0;
+    if (absv)
+      for (int d = 0; d < ORC_D_V; ++d) absv[(size_t)h * ORC_D_V + d] = 0.0;
   }
   /* pass 2: probability-weighted sum of V rows */
   for (int j = j0; j < j1; ++j) {
@@ -119,6 +123,10 @@ static int attend_range(const void* kv, int dtype, const int32_t* bt_row, int nu
       double p = scores[(size_t)h * n + (j - j0)];
       double* oh = o + (size_t)h * ORC_D_V;
       for (int d = 0; d < ORC_D_V; ++d) oh[d] += p * row[d];
+      if (absv) {
+        double* ah = absv + (size_t)h * ORC_D_V;
+        for (int d = 0; d < ORC_D_V; ++d) ah[d] += p * fabs(row[d]);
+      }
     }
   }
   return 0;
@@ -131,15 +139,18 @@ static int attend_range(const void* kv, int dtype, const int32_t* bt_row, int nu
  * seq_lens:   [B] int32
  * out:        [B, q_len, H, 512] fp64;  lse: [B, q_len, H] fp64
  * split_len:  0 = plain definition; > 0 = split/merge with chunks of that many keys
+ * absv:       optional [B, q_len, H, 512] fp64: sum_j softmax_j * |V_j[d]|, the scale of
+ *             the output's sensitivity to per-weight rounding (unsplit mode only)
  * Returns 0 on success, -1 on a block_table entry out of range, -2 on bad arguments.
  */
 int oracle_mla_decode(const void* q, const void* kv, int dtype, const int32_t* block_table, int max_pages,
                       const int32_t* seq_lens, int B, int q_len, int H, int num_pages, int page_size,
                       double softmax_scale, double q_scale, double kv_scale, int split_len,
-                      double* out, double* lse, int num_threads) {
+                      double* out, double* lse, double* absv, int num_threads) {
   if (!q || !kv || !block_table || !seq_lens || !out || !lse) return -2;
   if (dtype != ORC_BF16 && dtype != ORC_FP8_E4M3) return -2;
   if (B < 0 || q_len <= 0 || H <= 0 || page_size <= 0 || max_pages < 0 || split_len < 0) return -2;
+  if (absv && split_len > 0) return -2;
   for (int b = 0; b < B; ++b) {
     if (seq_lens[b] < 0 || (seq_lens[b] + page_size - 1) / page_size > max_pages) return -2;
   }
@@ -169,7 +180,7 @@ int oracle_mla_decode(const void* q, const void* kv, int dtype, const int32_t* b
     const int32_t* bt_row = block_table + (size_t)b * max_pages;
     if (split_len == 0) {
       if (attend_range(kv, dtype, bt_row, num_pages, page_size, 0, n, H, qv, softmax_scale, kv_scale, scores, row,
-                       o_acc, lse_acc) != 0)
+                       o_acc, lse_acc, absv ? absv + row0 * ORC_D_V : NULL) != 0)
         st = -1;
     } else {
       /* chunk partials, then the LSE-weighted merge */
@@ -180,7 +191,7 @@ int oracle_mla_decode(const void* q, const void* kv, int dtype, const int32_t* b
       for (int s = 0; s < nsplit && st == 0; ++s) {
         int j0 = s * chunk, j1 = j0 + chunk < n ? j0 + chunk : n;
         if (attend_range(kv, dtype, bt_row, num_pages, page_size, j0, j1, H, qv, softmax_scale, kv_scale, scores, row,
-                         all_o + (size_t)s * H * ORC_D_V, all_l + (size_t)s * H) != 0)
+                         all_o + (size_t)s * H * ORC_D_V, all_l + (size_t)s * H, NULL) != 0)
           st = -1;
       }
       for (int h = 0; h < H; ++h) {

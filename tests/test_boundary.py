@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/mla_decode.h declares, plans deterministically, and
+rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_paged_kv_decode_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(mla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mla.lib()
+    names = _declared_functions()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(mla.EXPORTS) == names
+    assert lib.mla_version() == 100
+
+
+def test_library_is_native_and_in_tree():
+    assert os.path.dirname(mla.LIB_PATH) == os.path.join(ROOT, "mla_paged_kv_decode_amd")
+    assert os.path.exists(mla.LIB_PATH)
+
+
+# ---------------------------------------------------------------- planning (host only)
+@pytest.mark.parametrize("B,q_len,H,L,F", [
+    (1, 1, 16, 256, 1),
+    (4, 4, 32, 81920, 4),
+    (16, 4, 32, 81920, 4),
+    (64, 1, 128, 65536, 1),
+    (128, 4, 64, 81920, 2),
+    (1, 3, 40, 900, 3),
+    (2, 1, 256, 700, 1),
+])
+def test_plan_fold_factor_and_workspace(B, q_len, H, L, F):
+    ns, fold, ws = mla.plan_for_cus(B, q_len, H, L, 256)
+    assert fold == F
+    assert ns >= 1
+    H_eff = H * F
+    U = (q_len // F) * ((H_eff + 127) // 128)
+    assert ns * U <= max(256, U)  # at most about one workgroup per compute unit
+    if ns > 1:
+        assert ns < 8 or ns % 8 == 0  # equal share per XCD once there are enough slices
+        rows = q_len * H
+        need = (ns + B) * rows * (512 * 4 + 4) + B * 8 + 8
+        assert need <= ws <= need + 3 * 256
+    else:
+        assert ws == 0
+    # cached/deterministic
+    assert mla.plan_for_cus(B, q_len, H, L, 256) == (ns, fold, ws)
+
+
+def test_plan_tiny_shape_needs_no_merge():
+    ns, fold, ws = mla.plan_for_cus(1, 1, 16, 256, 256)
+    assert (ns, ws) == (1, 0)
+
+
+def test_plan_options():
+    ns, fold, ws = mla.plan_for_cus(4, 4, 32, 81920, 256, mla.options(num_splits=24, partial_bf16=True, no_fold=True))
+    assert ns == 24 and fold == 1
+    rows = 4 * 32
+    assert ws >= (24 + 4) * rows * (512 * 2 + 4)
+
+
+def test_plan_rejects_bad_sizes():
+    for args in [(-1, 1, 1, 0), (1, 0, 1, 0), (1, 1, 0, 0), (1, 1, 1, -5)]:
+        with pytest.raises(mla.MlaError) as e:
+            mla.plan_for_cus(*args, 256)
+        assert e.value.code == -3
+
+
+# ---------------------------------------------------------------- validation before any device work
+def _shape(**kw):
+    s = mla.MlaShape()
+    s.batch, s.q_len, s.num_heads, s.num_pages, s.page_size, s.max_pages, s.max_seq_len, s.dtype = (
+        2, 4, 32, 100, 64, 10, 640, mla.DTYPE_FP8_E4M3)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def _decode_raw(shape, q=16, kv=16, bt=16, sl=16, out=16, lse=None, ws=None, wsb=0):
+    L = mla.lib()
+    return L.mla_decode(ctypes.byref(shape) if shape is not None else None, q, kv, bt, sl, 1.0, 1.0, 1.0, out, lse,
+                        ws, wsb, None)
+
+
+def test_validation_errors_without_device():
+    assert _decode_raw(None) == -1
+    assert _decode_raw(_shape(dtype=7)) == -2
+    assert _decode_raw(_shape(dtype=mla.DTYPE_FP16)) == -6
+    assert _decode_raw(_shape(page_size=48)) == -3
+    assert _decode_raw(_shape(page_size=8)) == -3
+    assert _decode_raw(_shape(q_len=0)) == -3
+    assert _decode_raw(_shape(num_pages=0)) == -3
+    assert _decode_raw(_shape(max_seq_len=641)) == -3
+    assert _decode_raw(_shape(), q=None) == -1
+    assert _decode_raw(_shape(), kv=24) == -4
+    assert _decode_raw(_shape(), out=8) == -4
+    assert _decode_raw(_shape(), bt=2) == -4
+    assert _decode_raw(_shape(batch=0)) == 0
+    msg = mla.lib().mla_last_error()
+    assert msg == b""
+    _decode_raw(_shape(page_size=48))
+    assert b"page_size" in mla.lib().mla_last_error()
+
+
+def test_pack_validation_without_device():
+    L = mla.lib()
+    assert L.mla_kv_pack_quantize_fp8(16, 512, 16, 64, None, -1, 1.0, 16, 10, None) == -3
+    assert L.mla_kv_pack_quantize_fp8(16, 500, 16, 64, None, 4, 1.0, 16, 10, None) == -3
+    assert L.mla_kv_pack_quantize_fp8(16, 516, 16, 64, None, 4, 1.0, 16, 10, None) == -4
+    assert L.mla_kv_pack_quantize_fp8(16, 512, 16, 64, None, 4, 0.0, 16, 10, None) == -3
+    assert L.mla_kv_pack_quantize_fp8(16, 512, 16, 64, None, 11, 1.0, 16, 10, None) == -3
+    assert L.mla_kv_pack_quantize_fp8(16, 512, 16, 64, None, 0, 1.0, 16, 10, None) == 0
+    assert L.mla_kv_pack_quantize_fp8(None, 512, 16, 64, None, 4, 1.0, 16, 10, None) == -1
+    assert L.mla_kv_pack_quantize_fp8(8, 512, 16, 64, None, 4, 1.0, 16, 10, None) == -4
+
+
+def test_device_query_fails_cleanly_without_gpu():
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(mla.MlaError) as e:
+        mla.plan(4, 4, 32, 81920)
+    assert e.value.code in (-8, -7)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(mla, "_lib", None)
+    monkeypatch.setattr(mla, "LIB_PATH", "/nonexistent/libmla_decode.so")
+    with pytest.raises(RuntimeError):
+        mla.lib()

@@ -1,0 +1,286 @@
+"""GPU parity of the HIP decode path against the fp64 oracle (needs an MI355X).
+
+Tolerances: bf16 O max-abs <= 1e-2, LSE <= 1e-3; FP8 O <= 5e-2 (the oracle
+runs on the dequantised FP8 values), LSE <= 1e-3.  Index handling (paging,
+masking, needles, page relabelling) is checked bit-exactly.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as mi
+import mla_paged_kv_decode_amd as mla
+from tests.gpu_util import assert_parity, out_f64, run_gpu, run_oracle, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# (B, q_len, H, dtype, lens, page_size): several tiles, ragged tails, every fold shape
+CASES = [
+    (1, 1, 16, mi.BF16, [256], 64),
+    (3, 4, 32, mi.FP8_E4M3, [0, 77, 1000], 64),
+    (3, 4, 32, mi.BF16, [5, 700, 64], 64),
+    (2, 1, 128, mi.BF16, [4096, 300], 64),
+    (2, 1, 128, mi.FP8_E4M3, [2113, 63], 64),
+    (2, 4, 64, mi.FP8_E4M3, [2000, 64], 64),
+    (2, 4, 64, mi.BF16, [1500, 3], 64),
+    (4, 2, 16, mi.FP8_E4M3, [1, 2, 3, 130], 16),
+    (4, 2, 16, mi.BF16, [1, 2, 3, 130], 16),
+    (1, 3, 40, mi.FP8_E4M3, [901], 32),
+    (1, 3, 40, mi.BF16, [901], 32),
+    (2, 1, 256, mi.FP8_E4M3, [700, 1200], 128),
+    (2, 2, 8, mi.BF16, [333, 2], 256),
+    (1, 5, 24, mi.FP8_E4M3, [600], 64),
+]
+
+
+@pytest.mark.parametrize("B,q_len,H,dtype,lens,ps", CASES)
+def test_parity_small(B, q_len, H, dtype, lens, ps):
+    x = mi.make_inputs(B, q_len, H, dtype, ("list", lens), page_size=ps, seed=100 + B * 7 + H + ps)
+    print(f"case B={B} q_len={q_len} H={H} dtype={dtype} lens={lens} ps={ps}", flush=True)
+    out, lse = run_gpu(x)
+    assert_parity(x, out, lse, run_oracle(x))
+
+
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+@pytest.mark.parametrize("splits", [1, 2, 3, 8, 64, 200])
+def test_forced_splits(dtype, splits):
+    x = mi.make_inputs(3, 4, 32, dtype, ("list", [2500, 90, 1300]), seed=31)
+    print(f"splits={splits} dtype={dtype}", flush=True)
+    out, lse = run_gpu(x, opts=mla.options(num_splits=splits))
+    assert_parity(x, out, lse, run_oracle(x))
+
+
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+def test_fold_and_partial_precision_options(dtype):
+    x = mi.make_inputs(2, 4, 16, dtype, ("list", [1800, 650]), seed=41)
+    ref = run_oracle(x)
+    base, lse_b = run_gpu(x)
+    nofold, lse_n = run_gpu(x, opts=mla.options(no_fold=True))
+    pb16, lse_p = run_gpu(x, opts=mla.options(partial_bf16=True, num_splits=16))
+    assert_parity(x, base, lse_b, ref)
+    assert_parity(x, nofold, lse_n, ref)
+    assert_parity(x, pb16, lse_p, ref, partial_bf16=True)
+    # folding only re-indexes rows: identical per-row arithmetic
+    assert torch.equal(base, nofold) and torch.equal(lse_b, lse_n)
+
+
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+def test_needles_are_bit_exact(dtype):
+    """One-hot queries pick exactly one visible key; a masked needle just past the limit is ignored."""
+    B, q_len, H, ps = 2, 4, 8, 64
+    lens = [300, 1025]
+    x = mi.make_inputs(B, q_len, H, dtype, ("list", lens), page_size=ps, seed=51)
+    x.softmax_scale, x.q_scale, x.kv_scale = 1.0, 1.0, 1.0
+    one = np.uint16(0x3F80) if dtype == mi.BF16 else np.uint8(0x38)     # 1.0
+    big = np.uint16(0x4400) if dtype == mi.BF16 else np.uint8(0x7E)     # 512.0 / 448.0
+    bigger = np.uint16(0x4480) if dtype == mi.BF16 else np.uint8(0x7E)  # masked needle at least as large
+    x.q[:] = 0
+    expected = {}
+    dims = [(t * H + h) % 576 for t in range(q_len) for h in range(H)]
+    for b in range(B):
+        L = lens[b]
+        for t in range(q_len):
+            for h in range(H):
+                x.q[b, t, h, (t * H + h) % 576] = one
+        # the needle dims are zero in every visible row of the sequence
+        pg = x.block_table[b, np.arange(L) // ps]
+        sl = np.arange(L) % ps
+        for d in dims:
+            x.kv_cache[pg, sl, d] = 0
+    for b in range(B):
+        L = lens[b]
+        for t in range(q_len):
+            n_t = L - q_len + t + 1
+            for h in range(H):
+                d = (t * H + h) % 576
+                # needle positions: start, a page boundary, the diagonal (last visible key)
+                j_star = [0, min(ps, n_t - 1), n_t - 1][(b + t + h) % 3]
+                x.kv_cache[x.block_table[b, j_star // ps], j_star % ps, d] = big
+                if n_t < L:  # a needle at least as large just past this token's limit must not be seen
+                    x.kv_cache[x.block_table[b, n_t // ps], n_t % ps, d] = bigger
+                expected[(b, t, h)] = j_star
+    out, lse = run_gpu(x)
+    O = out.cpu()
+    kv_t = torch.from_numpy(x.kv_cache.view(np.int16) if dtype == mi.BF16 else x.kv_cache)
+    kv_t = kv_t.view(torch.bfloat16 if dtype == mi.BF16 else torch.float8_e4m3fn)
+    for (b, t, h), j in expected.items():
+        v = kv_t[x.block_table[b, j // ps], j % ps, :512].float().to(torch.bfloat16)
+        assert torch.equal(O[b, t, h], v), (b, t, h, j)
+
+
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+def test_page_relabelling_bit_identical(dtype):
+    x = mi.make_inputs(3, 2, 32, dtype, ("list", [3000, 129, 2048]), seed=61)
+    out, lse = run_gpu(x)
+    perm = np.random.default_rng(2).permutation(x.num_pages)
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(perm.size)
+    x2 = mi.DecodeInputs(**{**x.__dict__})
+    x2.kv_cache = np.empty_like(x.kv_cache)
+    x2.kv_cache[inv] = x.kv_cache
+    x2.block_table = inv[x.block_table].astype(np.int32)
+    out2, lse2 = run_gpu(x2)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+def test_nan_poisoned_tails_and_spares_are_never_read(dtype):
+    x = mi.make_inputs(3, 4, 16, dtype, ("list", [70, 1, 1000]), page_size=64, seed=71, poison_tail=True)
+    out, lse = run_gpu(x)
+    assert_parity(x, out, lse, run_oracle(x))
+
+
+def test_zero_length_sequences_and_short_sequences():
+    x = mi.make_inputs(4, 4, 16, mi.FP8_E4M3, ("list", [0, 1, 3, 0]), page_size=16, seed=81)
+    out, lse = run_gpu(x)
+    assert_parity(x, out, lse, run_oracle(x))
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
+def test_output_guards_untouched():
+    x = mi.make_inputs(2, 4, 32, mi.BF16, ("list", [900, 40]), seed=91)
+    q, kv, bt, sl = to_dev(x)
+    B, ql, H = 2, 4, 32
+    guard = 7
+    out_buf = torch.full((B * ql * H * 512 + 2 * guard,), 12345.0, dtype=torch.bfloat16, device="cuda:0")
+    lse_buf = torch.full((B * ql * H + 2 * guard,), -777.0, dtype=torch.float32, device="cuda:0")
+    # 16-byte aligned interior views
+    out = out_buf[8:8 + B * ql * H * 512].view(B, ql, H, 512)
+    lse = lse_buf[guard:guard + B * ql * H].view(B, ql, H)
+    ns, ws = mla.plan(B, ql, H, x.max_seq_len)
+    ws_buf = torch.full((ws + 4096,), 0xA5, dtype=torch.uint8, device="cuda:0")
+    mla.decode(q, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_seq_len=x.max_seq_len, out=out, lse=lse,
+               workspace=ws_buf[:ws] if ws else ws_buf[:1])
+    torch.cuda.synchronize()
+    assert torch.all(out_buf[:8] == 12345.0) and torch.all(out_buf[8 + B * ql * H * 512:] == 12345.0)
+    assert torch.all(lse_buf[:guard] == -777.0) and torch.all(lse_buf[guard + B * ql * H:] == -777.0)
+    if ws:
+        assert torch.all(ws_buf[ws:] == 0xA5)
+    assert_parity(x, out, lse, run_oracle(x))
+
+
+def test_empty_batch_is_a_no_op():
+    x = mi.make_inputs(1, 1, 16, mi.BF16, ("list", [64]), seed=3)
+    q, kv, bt, sl = to_dev(x)
+    out = torch.full((0, 1, 16, 512), 1.0, dtype=torch.bfloat16, device="cuda:0")
+    mla.decode(q[:0], kv, bt[:0], sl[:0], 1.0, max_seq_len=0, out=out)
+    torch.cuda.synchronize()
+
+
+def test_workspace_errors():
+    x = mi.make_inputs(2, 4, 32, mi.BF16, ("list", [2000, 2000]), seed=4)
+    q, kv, bt, sl = to_dev(x)
+    ns, ws = mla.plan(2, 4, 32, 2000)
+    assert ns > 1 and ws > 0
+    small = torch.empty(ws - 256, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(mla.MlaError) as e:
+        mla.decode(q, kv, bt, sl, 1.0, max_seq_len=2000, workspace=small)
+    assert e.value.code == -5
+
+
+def test_hip_graph_replay_matches_eager():
+    """Capture one decode, then replay it with new seq_lens / block_table contents."""
+    # every block_table row holds valid pages for 2240 keys; replays use shorter lengths
+    x = mi.make_inputs(3, 4, 32, mi.FP8_E4M3, ("list", [2240, 2240, 2240]), seed=111)
+    q, kv, bt, sl = to_dev(x)
+    max_len = 2240
+    out = torch.empty(3, 4, 32, 512, dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.empty(3, 4, 32, dtype=torch.float32, device="cuda:0")
+    _, ws = mla.plan(3, 4, 32, max_len)
+    wsb = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda:0")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        mla.decode(q, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_seq_len=max_len, out=out, lse=lse,
+                   workspace=wsb)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mla.decode(q, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_seq_len=max_len, out=out, lse=lse,
+                   workspace=wsb)
+    rng = np.random.default_rng(5)
+    for rep in range(3):
+        lens = rng.integers(1, 2241, size=3).astype(np.int32)
+        sl.copy_(torch.from_numpy(lens))
+        x.seq_lens = lens
+        g.replay()
+        torch.cuda.synchronize()
+        got_o, got_l = out.clone(), lse.clone()
+        eager_o, eager_l = mla.decode(q, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_seq_len=max_len,
+                                      workspace=wsb)
+        torch.cuda.synchronize()
+        ref = run_oracle(x)
+        print(f"  rep {rep} lens {lens.tolist()}: eager", flush=True)
+        assert_parity(x, eager_o, eager_l, ref)
+        print(f"  rep {rep}: graph replay", flush=True)
+        assert_parity(x, got_o, got_l, ref)
+        assert torch.equal(got_o, eager_o) and torch.equal(got_l, eager_l), rep
+
+
+def test_kv_pack_quantize_bit_exact():
+    import oracle
+
+    rng = np.random.default_rng(13)
+    T = 333
+    latent = torch.from_numpy(rng.normal(0, 4, (T, 512)).astype(np.float32)).to(torch.bfloat16)
+    rope = torch.from_numpy(rng.normal(0, 4, (T, 64)).astype(np.float32)).to(torch.bfloat16)
+    latent[0, :6] = torch.tensor([1e6, -1e6, float("nan"), float("inf"), -0.0, 1e-30])
+    scale = 0.0123
+    ref = oracle.kv_pack_quantize_fp8(latent.view(torch.int16).numpy().view(np.uint16),
+                                      rope.view(torch.int16).numpy().view(np.uint16), scale)
+    got = mla.kv_pack_quantize_fp8(latent.cuda(), rope.cuda(), scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref)
+    # scattered into cache rows through a slot mapping (negative = skip)
+    slots = torch.from_numpy(rng.permutation(T + 50)[:T].astype(np.int64))
+    slots[3] = -1
+    cache = torch.zeros(T + 50, 576, dtype=torch.uint8, device="cuda:0")
+    mla.kv_pack_quantize_fp8(latent.cuda(), rope.cuda(), scale, slot_mapping=slots.cuda(), out=cache)
+    ref2 = oracle.kv_pack_quantize_fp8(latent.view(torch.int16).numpy().view(np.uint16),
+                                       rope.view(torch.int16).numpy().view(np.uint16), scale,
+                                       slot_mapping=slots.numpy(), num_rows=T + 50)
+    assert np.array_equal(cache.cpu().numpy(), ref2)
+
+
+def test_packed_cache_feeds_decode():
+    """Rows written by the pack kernel into a paged cache decode like the oracle says."""
+    import oracle
+
+    rng = np.random.default_rng(17)
+    B, L, H, ps = 2, 500, 32, 64
+    pages = (L + ps - 1) // ps
+    num_pages = B * pages + 3
+    T = B * L
+    latent = torch.from_numpy(rng.normal(0, 1, (T, 512)).astype(np.float32)).to(torch.bfloat16)
+    rope = torch.from_numpy(rng.normal(0, 1, (T, 64)).astype(np.float32)).to(torch.bfloat16)
+    kv_scale = 4.0 / 448.0
+    perm = rng.permutation(num_pages)[:B * pages].reshape(B, pages).astype(np.int32)
+    slots = np.array([perm[b, j // ps] * ps + j % ps for b in range(B) for j in range(L)], dtype=np.int64)
+    cache = torch.zeros(num_pages * ps, 576, dtype=torch.uint8, device="cuda:0")
+    mla.kv_pack_quantize_fp8(latent.cuda(), rope.cuda(), kv_scale, slot_mapping=torch.from_numpy(slots).cuda(),
+                             out=cache)
+    q32 = rng.normal(0, 1, (B, 4, H, 576)).astype(np.float32)
+    q_scale = float(np.abs(q32).max() / 448.0)
+    qc = torch.from_numpy(q32 / q_scale).clamp(-448, 448).to(torch.float8_e4m3fn)
+    x = mi.DecodeInputs(q=qc.view(torch.uint8).numpy(), kv_cache=cache.cpu().numpy().reshape(num_pages, ps, 576),
+                        block_table=perm, seq_lens=np.full(B, L, np.int32), dtype=mi.FP8_E4M3, q_scale=q_scale,
+                        kv_scale=kv_scale, softmax_scale=1 / math.sqrt(192), page_size=ps)
+    out, lse = run_gpu(x)
+    assert_parity(x, out, lse, run_oracle(x))
+
+
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+def test_empty_slices_ignore_stale_workspace(dtype):
+    """More KV slices than 64-key units: empty slices write nothing and the merge must skip them."""
+    x = mi.make_inputs(3, 4, 32, dtype, ("list", [700, 5, 130]), seed=121)
+    q, kv, bt, sl = to_dev(x)
+    opts = mla.options(num_splits=96)
+    _, ws = mla.plan(3, 4, 32, x.max_seq_len, opts)
+    wsb = torch.full((ws,), 0xFF, dtype=torch.uint8, device="cuda:0")  # NaN everywhere
+    out, lse = mla.decode(q, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_seq_len=x.max_seq_len,
+                          workspace=wsb, opts=opts)
+    torch.cuda.synchronize()
+    assert_parity(x, out, lse, run_oracle(x))

@@ -233,3 +233,19 @@ def test_kv_pack_quantize_matches_torch_cast():
                                        num_rows=T + 10)
     assert np.array_equal(got2[5], ref[0]) and np.array_equal(got2[7:7 + T - 2], ref[2:])
     assert not got2[6].any()
+
+
+def test_weighted_abs_v_matches_brute_force():
+    x = mi.make_inputs(2, 4, 3, mi.FP8_E4M3, ("list", [33, 140]), page_size=16, seed=14)
+    O, lse, absv = _run(x, want_absv=True)
+    q = decode_values(x.q, x.dtype) * x.q_scale
+    kv = decode_values(x.kv_cache, x.dtype) * x.kv_scale
+    for b, L in enumerate([33, 140]):
+        K = dense_keys(kv, x.block_table, b, L)
+        for t in range(4):
+            n_t = L - 4 + t + 1
+            s = x.softmax_scale * q[b, t] @ K[:n_t].T
+            w = np.exp(s - s.max(axis=-1, keepdims=True))
+            w /= w.sum(axis=-1, keepdims=True)
+            assert np.allclose(absv[b, t], w @ np.abs(K[:n_t, :512]), rtol=1e-12, atol=1e-15)
+    assert np.all(absv >= np.abs(O) - 1e-12)
