@@ -104,7 +104,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--num-splits", type=int, default=0, help="override the planned KV slice count")
-    ap.add_argument("--partial-bf16", action="store_true")
+    ap.add_argument("--partial-fp32", action="store_true", help="keep split partials in fp32 (default bf16)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -135,14 +135,14 @@ def main():
     B, q_len, H = x.B, x.q_len, x.H
     out = torch.empty(B, q_len, H, 512, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(B, q_len, H, dtype=torch.float32, device=dev)
-    base_opts = mla.options(num_splits=args.num_splits, partial_bf16=args.partial_bf16)
+    base_opts = mla.options(num_splits=args.num_splits, partial_fp32=args.partial_fp32)
     num_splits, ws_bytes = mla.plan(B, q_len, H, x.max_seq_len, base_opts)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     del x.kv_cache  # host copy no longer needed (the CPU baseline regenerates if asked)
 
     def step(i, split_event=None):
-        opts = mla.options(num_splits=args.num_splits, partial_bf16=args.partial_bf16, split_event=split_event)
+        opts = mla.options(num_splits=args.num_splits, partial_fp32=args.partial_fp32, split_event=split_event)
         mla.decode(q, kvs[i % copies], bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_seq_len=x.max_seq_len,
                    out=out, lse=lse, workspace=ws, opts=opts, stream=stream.cuda_stream)
 

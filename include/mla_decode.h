@@ -139,7 +139,7 @@ int mla_decode(const mla_shape* shape, const void* q, const void* kv_cache, cons
 typedef struct mla_options {
   int32_t num_splits;   /* > 0: use this many KV slices instead of the planned count */
   int32_t no_fold;      /* != 0: do not fold query tokens into heads (F = 1) */
-  int32_t partial_bf16; /* != 0: keep the split partial outputs as bf16 instead of fp32 */
+  int32_t partial_fp32; /* != 0: keep the split partial outputs in fp32 (default: bf16) */
   int32_t reserved[5];
   void* split_event;    /* hipEvent_t or NULL: recorded on `stream` after the split-KV kernel
                            and before the merge kernel, so callers can time each kernel */

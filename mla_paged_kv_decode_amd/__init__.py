@@ -45,16 +45,16 @@ class MlaShape(ctypes.Structure):
 
 
 class MlaOptions(ctypes.Structure):
-    _fields_ = [("num_splits", ctypes.c_int32), ("no_fold", ctypes.c_int32), ("partial_bf16", ctypes.c_int32),
+    _fields_ = [("num_splits", ctypes.c_int32), ("no_fold", ctypes.c_int32), ("partial_fp32", ctypes.c_int32),
                 ("reserved", ctypes.c_int32 * 5), ("split_event", ctypes.c_void_p)]
 
 
-def options(num_splits: int = 0, no_fold: bool = False, partial_bf16: bool = False, split_event=None) -> MlaOptions:
+def options(num_splits: int = 0, no_fold: bool = False, partial_fp32: bool = False, split_event=None) -> MlaOptions:
     """mla_options; split_event is a raw hipEvent_t (e.g. torch.cuda.Event().cuda_event after one record)."""
     o = MlaOptions()
     o.num_splits = int(num_splits)
     o.no_fold = int(bool(no_fold))
-    o.partial_bf16 = int(bool(partial_bf16))
+    o.partial_fp32 = int(bool(partial_fp32))
     o.split_event = split_event
     return o
 

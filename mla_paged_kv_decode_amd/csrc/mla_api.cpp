@@ -65,7 +65,7 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int num_cus, const mla_
   pl.q_len_eff = q_len / pl.F;
   pl.m_tiles = (pl.H_eff + mla::kTileM - 1) / mla::kTileM;
   pl.U = pl.q_len_eff * pl.m_tiles;
-  pl.part_bf16 = (opt && opt->partial_bf16) ? 1 : 0;
+  pl.part_bf16 = (opt && opt->partial_fp32) ? 0 : 1;
   const long long units_per_seq = max_seq_len > 0 ? (max_seq_len + mla::kUnitKeys - 1) / mla::kUnitKeys : 1;
   const long long units_max = (long long)B * units_per_seq;
   int G;
@@ -140,7 +140,7 @@ int check_plan_args(int B, int q_len, int H, int max_seq_len) {
 
 int cached_plan(int dev, int cus, int B, int q_len, int H, int max_seq_len, const mla_options* opt, Plan* out) {
   const auto key = std::make_tuple(dev, B, q_len, H, max_seq_len, opt ? opt->num_splits : 0, opt ? opt->no_fold : 0,
-                                   opt ? opt->partial_bf16 : 0, cus);
+                                   opt ? opt->partial_fp32 : 0, cus);
   std::lock_guard<std::mutex> lk(g_mu);
   auto it = g_plans.find(key);
   if (it == g_plans.end()) it = g_plans.emplace(key, make_plan(B, q_len, H, max_seq_len, cus, opt)).first;

@@ -39,6 +39,22 @@ typedef __attribute__((address_space(4))) const int32_t cint_t;
 constexpr float kTau = 32.0f;  // rescale the accumulators only when a row max grows by more (log2 units)
 constexpr float kLn2 = 0.693147180559945309417f;
 constexpr int kDmaPerWave = kStageBytes / 1024 / 4;  // 9 one-KiB LDS writes per wave per tile
+// Epilogue staging: per wave 32 rows of 256 columns; row pitches padded by 8
+// (bf16) / 16 (fp32) bytes so column-wise writes of 32 rows hit distinct banks.
+constexpr int kEpiRowB16 = 256 * 2 + 8;
+constexpr int kEpiRowF32 = 256 * 4 + 16;
+constexpr int kEpiWaveBytes = 32 * kEpiRowF32;
+static_assert(4 * kEpiWaveBytes <= kStages * kStageBytes, "epilogue staging must fit in the KV ring");
+// 1 KiB LDS scratch after the ring: destination of the loads of dummy tiles
+constexpr int kDummyOffset = kStages * kStageBytes;
+// fp8 path: P of the four row blocks (B-operand layout, 2 KiB each) and their
+// per-row MFMA scales (4 per lane), shared by all waves
+constexpr int kPOffset = kDummyOffset + 1024;
+constexpr int kPScaleOffset = kPOffset + 4 * 2048;
+constexpr int kLdsBytes = kPScaleOffset + 1024;
+// fp8 epilogue staging: 128 rows, pitch 1 KiB + 16 bytes
+constexpr int kEpiPitch = 1024 + 16;
+static_assert(kTileM * kEpiPitch <= kStages * kStageBytes, "epilogue staging must fit in the KV ring");
 
 template <int DT>
 struct Traits;
@@ -104,20 +120,57 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // Score MFMAs are issued through asm so that their accumulators stay in
 // VGPRs: the compiler otherwise selects the AGPR form for every MFMA of the
 // kernel, and the 256 AGPRs are exactly the 32x512 fp32 output accumulator.
-// The compiler does not model hazards of asm MFMAs, so each one starts with
-// a short s_nop (VALU-written operands) and the chain ends with qk_fence()
-// before any VALU reads the accumulators.
-__device__ __forceinline__ void qk_mfma_f8(v16f& acc, const v8i& a, const v8i& b, int sc) {
-  asm("s_nop 2\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
-      : "+v"(acc)
-      : "v"(a), "v"(b), "v"(sc));
+// The compiler does not model hazards of asm MFMAs and takes their results as
+// written when the asm issues, while the hardware writes them some 64 cycles
+// later.  Each MFMA therefore starts with a short s_nop (VALU-written
+// operands), and the last MFMA of a chain carries the wait states that must
+// pass before anything (a VALU use, or a copy the register allocator may
+// insert) reads the accumulator, inside the same asm statement.
+__device__ __forceinline__ void qk_mfma_f8(v16f& acc, const v8i& a, const v8i& b, bool last) {
+  if (last) {
+    asm volatile(
+        "s_nop 2\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]\n\t"
+        "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+        : "+v"(acc)
+        : "v"(a), "v"(b), "v"(127));
+  } else {
+    asm volatile("s_nop 2\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+                 : "+v"(acc)
+                 : "v"(a), "v"(b), "v"(127));
+  }
 }
-__device__ __forceinline__ void qk_mfma_bf16(v16f& acc, const v4i& a, const v4i& b) {
-  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+// first MFMA of a chain: accumulator input is zero.  The output is early-clobber:
+// a multi-pass MFMA must not write registers that hold its own A or B operand.
+__device__ __forceinline__ void qk_mfma_f8_first(v16f& acc, const v8i& a, const v8i& b) {
+  asm volatile("s_nop 2\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0]"
+               : "=&v"(acc)
+               : "v"(a), "v"(b), "v"(127));
 }
-__device__ __forceinline__ void qk_fence(v16f& a) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a)); }
-__device__ __forceinline__ void qk_fence(v16f& a, v16f& b) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b));
+__device__ __forceinline__ void qk_mfma_bf16(v16f& acc, const v4i& a, const v4i& b, bool last) {
+  if (last) {
+    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+v"(acc)
+                 : "v"(a), "v"(b));
+  } else {
+    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  }
+}
+// Scheduling fences.  The instruction selector places pure arithmetic next to
+// its uses, regardless of where the source puts it; routing a slot's inputs
+// and outputs through empty volatile asm statements pins that work between
+// the MFMAs it is meant to overlap.
+template <typename T>
+__device__ __forceinline__ void fence_v(T& x) {
+  asm volatile("" : "+v"(x));
+}
+// max / sum of a value with the one held 32 lanes away (v_permlane32_swap)
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Keep a 16-float accumulator block in AGPRs: values defined by VALU code
@@ -183,6 +236,11 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   constexpr int CH = TR::kChunks;
   constexpr int ESZ = (DT == kFp8) ? 1 : 2;
 
+  // Opaque copies of the lane and wave ids: everything derived from them is
+  // computed inside this segment instead of being hoisted above the caller's
+  // segment loop, where it would stay live (and spill) across the whole kernel.
+  asm volatile("" : "+v"(lane));
+  asm volatile("" : "+s"(wave));
   const int n = lane & 31;
   const int hh = lane >> 5;
   cint_t* seq_lens = (cint_t*)p.seq_lens;
@@ -225,6 +283,10 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
     }
   }
 
+  // Q must be in registers before the KV ring starts: the compiler cannot see the
+  // asynchronous LDS loads, so its own wait for Q would otherwise drain the ring.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0), expcnt/lgkmcnt unconstrained
+
   v16f o[16];
   float m_ref = -INFINITY;  // reference the accumulators are relative to (log2 units)
   float l_acc = 0.f;        // this lane's share of sum exp2(s - m_ref)
@@ -243,69 +305,94 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
     const uint32_t smem_base = lds_addr(smem);
 
     // Per-lane DMA geometry: wave instruction kk writes LDS chunk slots
-    // [64*(wave+4kk), +64); lane -> slot -> (row, source chunk).  The nine
-    // byte offsets row*RB + chunk*16 (< 2^16) are kept as packed halves.
-    auto dma_row = [&](int kk) -> int { return (64 * (wave + 4 * kk) + lane) / CH; };
-    auto dma_col = [&](int kk) -> int {
+    // [64*(wave+4kk), +64); lane -> slot -> (row, source chunk), kept packed
+    // as row << 16 | (row*RB + chunk*16) (that byte offset is below 2^16).
+    uint32_t dgeo[kDmaPerWave];
+#pragma unroll
+    for (int kk = 0; kk < kDmaPerWave; ++kk) {
       const int slot = 64 * (wave + 4 * kk) + lane;
       const int row = slot / CH;
-      return ((slot - row * CH) ^ swz<DT>(row)) * 16;
-    };
-    uint32_t dofs[(kDmaPerWave + 1) / 2];
-#pragma unroll
-    for (int i = 0; i < (kDmaPerWave + 1) / 2; ++i) {
-      const uint32_t lo = (uint32_t)(dma_row(2 * i) * RB + dma_col(2 * i));
-      const uint32_t hi = (2 * i + 1 < kDmaPerWave) ? (uint32_t)(dma_row(2 * i + 1) * RB + dma_col(2 * i + 1)) : 0u;
-      dofs[i] = lo | (hi << 16);
+      const int col = ((slot - row * CH) ^ swz<DT>(row)) * 16;
+      dgeo[kk] = ((uint32_t)row << 16) | (uint32_t)(row * RB + col);
     }
 
-    auto page_of = [&](int pidx) -> int {
-      int pg = bt[min(pidx, plast)];
-      return min(max(pg, 0), p.num_pages - 1);
-    };
+    auto page_raw = [&](int pidx) -> int { return bt[min(pidx, plast)]; };
+    auto clamp_page = [&](int pg) -> int { return min(max(pg, 0), p.num_pages - 1); };
 
-    // Issue the DMA of tile `tt` (segment-relative) into its ring stage.
-    auto issue_tile = [&](int tt) {
-      const int key0 = k0 + tt * TILE;
-      const uint32_t m0_stage = smem_base + (uint32_t)((tt % kStages) * kStageBytes);
-      const bool tail = key0 + TILE > k1;
+    // Scalar state of the tile whose loads are being issued.  Block-table
+    // entries are read one tile ahead, so the scalar-load wait lands at the
+    // top of an iteration rather than inside an MFMA chain.  A tile index past
+    // the segment sets up a dummy tile: its loads re-read row 0 of the last
+    // real tile (an L2 hit) into a 1 KiB scratch area of LDS, which keeps the
+    // number of loads per iteration, and hence every vmcnt wait, uniform.
+    const uint8_t* d_base = p.kv;
+    uint32_t d_m0 = smem_base, d_step = 1024;
+    int d_nvalid = 0, d_key0 = k0, d_pidx0 = 0;
+    int d_pg0 = 0, d_pg1 = 0, d_pg2 = 0, d_pg3 = 0;
+    int pf0 = 0, pf1 = 0, pf2 = 0, pf3 = 0;
+    auto prefetch_pages = [&](int tt) {
+      const int pidx0 = (k0 + tt * TILE) >> p.page_shift;
+      pf0 = page_raw(pidx0);
+      if constexpr (!FAST) {
+        pf1 = page_raw(pidx0 + 1);
+        pf2 = page_raw(pidx0 + 2);
+        pf3 = page_raw(pidx0 + 3);
+      }
+    };
+    auto dma_setup = [&](int tt) {
+      if (tt < ntiles) {
+        const int key0 = k0 + tt * TILE;
+        d_m0 = smem_base + (uint32_t)((tt % kStages) * kStageBytes);
+        d_step = 1024;
+        d_nvalid = min(TILE, k1 - key0);
+        d_key0 = key0;
+        d_pidx0 = key0 >> p.page_shift;
+        if constexpr (FAST) {
+          d_base = p.kv + ((size_t)clamp_page(pf0) * p.page_size + (key0 & pmask)) * RB;
+        } else {
+          d_pg0 = clamp_page(pf0);
+          d_pg1 = clamp_page(pf1);
+          d_pg2 = clamp_page(pf2);
+          d_pg3 = clamp_page(pf3);
+        }
+        if (tt + 1 < ntiles) prefetch_pages(tt + 1);
+      } else {
+        d_m0 = smem_base + (uint32_t)kDummyOffset;
+        d_step = 0;
+        d_nvalid = 0;
+      }
+    };
+    // load kk (of kDmaPerWave) of this wave for the tile set up last
+    auto dma_issue = [&](int kk) {
+      const uint32_t g = dgeo[kk];
+      const int row = (int)(g >> 16);
+      const uint32_t off = g & 0xffffu;
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(d_m0 + d_step * (uint32_t)(wave + 4 * kk));
+      // fp8 tiles are loaded whole and their rows past the segment's last key
+      // are zeroed in LDS afterwards (zero_tail); bf16 tiles re-read row 0 there.
+      constexpr bool kClampRows = DT != kFp8;
       if constexpr (FAST) {
         // page_size >= TILE: the tile is TILE consecutive rows of one page
-        const int pg = page_of(key0 >> p.page_shift);
-        const int rip = key0 & pmask;
-        const uint8_t* sbase = p.kv + ((size_t)pg * p.page_size + rip) * RB;
-        if (!tail) {
-#pragma unroll
-          for (int kk = 0; kk < kDmaPerWave; ++kk) {
-            const uint32_t off = (dofs[kk >> 1] >> (16 * (kk & 1))) & 0xffffu;
-            const uint32_t m0 = m0_stage + (uint32_t)(1024 * (wave + 4 * kk));
-            dma16_sbase(off, sbase, __builtin_amdgcn_readfirstlane(m0));
-          }
-        } else {
-          // rows past the segment's last key re-read row 0 (finite data, masked later)
-#pragma unroll
-          for (int kk = 0; kk < kDmaPerWave; ++kk) {
-            const int row = dma_row(kk);
-            const uint32_t off = (uint32_t)((key0 + row >= k1 ? 0 : row * RB) + dma_col(kk));
-            const uint32_t m0 = m0_stage + (uint32_t)(1024 * (wave + 4 * kk));
-            dma16_sbase(off, sbase, __builtin_amdgcn_readfirstlane(m0));
-          }
-        }
+        const uint32_t voff = (!kClampRows || row < d_nvalid) ? off : off - (uint32_t)(row * RB);
+        dma16_sbase(voff, d_base, m0);
       } else {
         // page_size < TILE: up to four pages per tile
-        const int pidx0 = key0 >> p.page_shift;
-        const int pg0 = page_of(pidx0), pg1 = page_of(pidx0 + 1), pg2 = page_of(pidx0 + 2), pg3 = page_of(pidx0 + 3);
-#pragma unroll
-        for (int kk = 0; kk < kDmaPerWave; ++kk) {
-          int key = key0 + dma_row(kk);
-          if (key >= k1) key = key0;
-          const int rel = (key >> p.page_shift) - pidx0;
-          const int pg = rel == 0 ? pg0 : rel == 1 ? pg1 : rel == 2 ? pg2 : pg3;
-          const uint8_t* src = p.kv + ((size_t)pg * p.page_size + (key & pmask)) * RB + dma_col(kk);
-          const uint32_t m0 = m0_stage + (uint32_t)(1024 * (wave + 4 * kk));
-          dma16_vaddr(src, __builtin_amdgcn_readfirstlane(m0));
-        }
+        const int key = d_key0 + ((!kClampRows || row < d_nvalid) ? row : 0);
+        const int rel = (key >> p.page_shift) - d_pidx0;
+        // readfirstlane (a no-op on these uniform values) keeps the per-lane select
+        // a select of values: a select of loads would be folded into a load through
+        // a selected address, which pins the captured variables in private memory
+        const int g0 = __builtin_amdgcn_readfirstlane(d_pg0), g1 = __builtin_amdgcn_readfirstlane(d_pg1);
+        const int g2 = __builtin_amdgcn_readfirstlane(d_pg2), g3 = __builtin_amdgcn_readfirstlane(d_pg3);
+        const int pg = rel == 0 ? g0 : rel == 1 ? g1 : rel == 2 ? g2 : g3;
+        const uint8_t* src = p.kv + ((size_t)pg * p.page_size + (key & pmask)) * RB + (off - (uint32_t)(row * RB));
+        dma16_vaddr(src, m0);
       }
+    };
+    auto issue_tile = [&](int tt) {
+      dma_setup(tt);
+#pragma unroll
+      for (int kk = 0; kk < kDmaPerWave; ++kk) dma_issue(kk);
     };
 
     // smallest visible limit over the wave's rows: tiles below it need no mask
@@ -359,177 +446,367 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
       }
       // all waves are done with the previous use of the LDS ring
       lds_barrier();
+      prefetch_pages(0);
+
+      if constexpr (DT == kFp8) {
+        // Software pipeline, iteration t (one 64-key tile):
+        //   wait for tile t; set up the loads of tile t+2;
+        //   score MFMAs of tile t, interleaved with the loads of tile t+2 and
+        //     the second half of tile t-1's softmax (keys 32..63);
+        //   PV MFMAs of tile t-1, interleaved with the first half of tile t's
+        //     softmax (row max, scale, keys 0..31).
+        // Ring stages in use during iteration t: t-1 (PV), t (scores), t+1 and
+        // t+2 (loads in flight).  LDS operands are read three MFMAs ahead.
+        auto kread = [&](const lds_t* st, int c, int kb) -> v8i {
+          const v4i x = *(const lds_v4i*)(st + kaddr[0] + 64 * c + 32 * RB * kb);
+          const v4i y = *(const lds_v4i*)(st + kaddr[1] + 64 * c + 32 * RB * kb);
+          return v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        };
+        auto vread = [&](const lds_t* st, int db) -> v8i {
+          const int base = vaddr[db & 1] + 64 * (db >> 1);
+          const v2i r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(st + base));
+          const v2i r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(st + base + 16 * RB));
+          const v2i r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(st + base + 32 * RB));
+          const v2i r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(st + base + 48 * RB));
+          return v8i{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+        };
+        v16f s0, s1;            // scores of the tile passing through the score MFMAs
+        v16f hb;                // keys 32..63 of the previous tile's scores
+        int pa[4], pb[4];       // fp8 P words: keys 0..31 and 32..63
+        float pe_off = 0.f;     // exp2 offset of the tile whose P is being built
+        int pe_e = 0;           // its power-of-two scale
+        float lsum = 0.f, mx_raw = -INFINITY, p_hold = 0.f;
+        int w_hold = 0;
+
+        // softmax, first half (PV slots 0..15): row max over the tile (tree, two
+        // slots), reference and scale (two slots), then P of keys 0..31 (two
+        // elements per slot in slots 4..7, one in slots 8..15)
+        float mx0 = -INFINITY;
+        auto max16 = [&](const v16f& x) -> float {
+          const float a0 = fmaxf(fmaxf(x[0], x[1]), x[2]), a1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+          const float a2 = fmaxf(fmaxf(x[6], x[7]), x[8]), a3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
+          const float a4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
+          return fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), x[15]));
+        };
+        auto p_elem = [&](int idx) -> float {
+          return __builtin_amdgcn_exp2f(__builtin_fmaf(s0[idx], p.s_scale_log2, -pe_off));
+        };
+        auto part_a = [&](int slot, int key0, bool need_mask) {
+          if (slot == 0) {
+            if (need_mask) {
 #pragma unroll
-      for (int s = 0; s < kStages - 1; ++s)
-        if (s < ntiles) issue_tile(s);
-
-      for (int tt = 0; tt < ntiles; ++tt) {
-        wait_tile_barrier(min(kStages - 2, ntiles - 1 - tt));
-        if (tt + kStages - 1 < ntiles) issue_tile(tt + kStages - 1);
-        if (!wave_active) continue;
-
-        const lds_t* st = smem + (tt % kStages) * kStageBytes;
-        const int key0 = k0 + tt * TILE;
-        const bool need_mask = key0 + TILE > lim_min;
-
-        if constexpr (DT == kFp8) {
-          // ---- S^T = K Q^T : two 32-key blocks, K = 576 in 9 steps of 64 ----
-          // one step of LDS reads in flight ahead of the MFMAs
-          auto kread = [&](int c, int kb) -> v8i {
-            const v4i x = *(const lds_v4i*)(st + kaddr[0] + 64 * c + 32 * RB * kb);
-            const v4i y = *(const lds_v4i*)(st + kaddr[1] + 64 * c + 32 * RB * kb);
-            return v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-          };
-          v16f s0 = v16f{0}, s1 = v16f{0};
-          v8i a0 = kread(0, 0), a1 = kread(0, 1);
-#pragma unroll
-          for (int c = 0; c < 9; ++c) {
-            v8i n0 = a0, n1 = a1;
-            if (c + 1 < 9) {
-              n0 = kread(c + 1, 0);
-              n1 = kread(c + 1, 1);
+              for (int r = 0; r < 16; ++r) {
+                const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                if (key >= lim) s0[r] = -INFINITY;
+                if (key + 32 >= lim) s1[r] = -INFINITY;
+              }
             }
-            qk_mfma_f8(s0, a0, qreg[c], 127);
-            qk_mfma_f8(s1, a1, qreg[c], 127);
+            fence_v(s0);
+            mx0 = max16(s0);
+            fence_v(mx0);
+          } else if (slot == 1) {
+            fence_v(s1);
+            mx_raw = fmaxf(mx0, max16(s1));
+            fence_v(mx_raw);
+          } else if (slot == 2) {
+            const float mx = mx_raw * p.s_scale_log2;  // lane max, log2 units
+            mx_raw = xor32_max(mx);                     // row max of the tile
+            m_seen = fmaxf(m_seen, mx_raw);
+            if (m_ref == -INFINITY) m_ref = mx_raw;
+            ovf = ovf || (mx_raw > m_ref + kTau);
+            fence_v(mx_raw);
+            fence_v(m_seen);
+            fence_v(m_ref);
+          } else if (slot == 3) {
+            const float rm = mx_raw;
+            const float mref = m_ref > -INFINITY ? m_ref : 0.f;
+            // power-of-two block scale per query row: the row's largest p of this tile lands
+            // in (128, 256].  The MFMA's 32-element scale blocks of a column interleave both
+            // lane halves (bytes 0-15 of lanes n and n+32 take lane n's scale, bytes 16-31
+            // take lane n+32's), so both halves of a row must carry the same scale.
+            int e = 0;
+            if (rm > -INFINITY) e = 8 - (int)ceilf(rm - mref);
+            e = min(max(e, -120), 120);
+            pe_e = e;
+            pe_off = mref - (float)e;
+            lsum = 0.f;
+            fence_v(pe_off);
+            fence_v(pe_e);
+          } else if (slot >= 4 && slot < 8) {
+            const int q = slot - 4;  // elements 2q, 2q+1 of s0
+            fence_v(s0);
+            const float p0 = p_elem(2 * q), p1 = p_elem(2 * q + 1);
+            lsum += p0 + p1;
+            fence_v(lsum);
+            if ((q & 1) == 0) {
+              w_hold = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+              fence_v(w_hold);
+            } else {
+              pa[q >> 1] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, w_hold, true);
+              fence_v(pa[q >> 1]);
+            }
+          } else if (slot >= 8) {
+            const int idx = slot;  // elements 8..15 of s0, one per slot
+            fence_v(s0);
+            const float pv = p_elem(idx);
+            lsum += pv;
+            fence_v(lsum);
+            const int j = idx & 3;
+            if (j == 0 || j == 2) {
+              p_hold = pv;
+              fence_v(p_hold);
+            } else if (j == 1) {
+              w_hold = __builtin_amdgcn_cvt_pk_fp8_f32(p_hold, pv, 0, false);
+              fence_v(w_hold);
+            } else {
+              pa[idx >> 2] = __builtin_amdgcn_cvt_pk_fp8_f32(p_hold, pv, w_hold, true);
+              fence_v(pa[idx >> 2]);
+            }
+          }
+        };
+        // softmax, second half: P of keys 32..63 (from hb), then the row sum
+        auto part_b = [&](int slot) {
+          if (slot < 16) {
+            fence_v(hb);  // (in place: no copy)
+            const float x = hb[slot];
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.s_scale_log2, -pe_off));
+            lsum += pv;
+            fence_v(lsum);
+            const int j = slot & 3;
+            if (j == 0 || j == 2) {
+              p_hold = pv;
+              fence_v(p_hold);
+            } else if (j == 1) {
+              w_hold = __builtin_amdgcn_cvt_pk_fp8_f32(p_hold, pv, 0, false);
+              fence_v(w_hold);
+            } else {
+              pb[slot >> 2] = __builtin_amdgcn_cvt_pk_fp8_f32(p_hold, pv, w_hold, true);
+              fence_v(pb[slot >> 2]);
+            }
+          } else if (slot == 16) {
+            l_acc += __builtin_ldexpf(lsum, -pe_e);
+            fence_v(l_acc);
+          }
+        };
+        // S^T = K Q^T for one tile: two 32-key blocks, K = 576 in 9 steps of 64
+        auto qk_chain = [&](const lds_t* st, bool with_b) {
+          if constexpr (!FAST) {
+#pragma unroll
+            for (int kk = 0; kk < kDmaPerWave; ++kk) dma_issue(kk);
+          }
+          v8i kb[4];
+          kb[0] = kread(st, 0, 0);
+          kb[1] = kread(st, 0, 1);
+          kb[2] = kread(st, 1, 0);
+#pragma unroll
+          for (int i = 0; i < 18; ++i) {
+            if (i + 3 < 18) kb[(i + 3) & 3] = kread(st, (i + 3) >> 1, (i + 3) & 1);
+            if (i & 1) {
+              if (i == 1) {
+                qk_mfma_f8_first(s1, kb[i & 3], qreg[i >> 1]);
+              } else {
+                qk_mfma_f8(s1, kb[i & 3], qreg[i >> 1], i == 17);
+              }
+              if constexpr (FAST) dma_issue(i >> 1);
+            } else {
+              if (i == 0) {
+                qk_mfma_f8_first(s0, kb[i & 3], qreg[i >> 1]);
+              } else {
+                qk_mfma_f8(s0, kb[i & 3], qreg[i >> 1], i == 16);
+              }
+            }
+            if (with_b) part_b(i);
             __builtin_amdgcn_sched_barrier(0);
-            a0 = n0;
-            a1 = n1;
           }
-          qk_fence(s0, s1);
-          // ---- mask, softmax numerators (base 2) ----
-          if (need_mask) {
+        };
+        // this wave's P (its 32 rows, B-operand layout) and per-row scale into LDS
+        auto p_publish = [&]() {
+          lds_t* pw = smem + kPOffset + wave * 2048;
+          *(lds_v4i*)(pw + 16 * lane) = v4i{pa[0], pa[1], pa[2], pa[3]};
+          *(lds_v4i*)(pw + 1024 + 16 * lane) = v4i{pb[0], pb[1], pb[2], pb[3]};
+          *(__attribute__((address_space(3))) int*)(smem + kPScaleOffset + 16 * lane + 4 * wave) = 127 - pe_e;
+        };
+        // O^T += V^T P^T for this wave's 128 latent dims (4 blocks of 32) and all
+        // four row blocks: each transposed V read feeds four MFMAs
+        auto pv_chain = [&](const lds_t* st, bool with_a, int key0, bool need_mask) {
+          v8i pt[4];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = key0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-              if (key >= lim) s0[i] = -INFINITY;
-              if (key + 32 >= lim) s1[i] = -INFINITY;
+          for (int r = 0; r < 4; ++r) {
+            const v4i x = *(const lds_v4i*)(smem + kPOffset + r * 2048 + 16 * lane);
+            const v4i y = *(const lds_v4i*)(smem + kPOffset + r * 2048 + 1024 + 16 * lane);
+            pt[r] = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+          }
+          const v4i psc = *(const lds_v4i*)(smem + kPScaleOffset + 16 * lane);
+          v8i vb[2];
+          vb[0] = vread(st, 4 * wave);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (r == 0 && j + 1 < 4) vb[(j + 1) & 1] = vread(st, 4 * wave + j + 1);
+              fence_v(vb[j & 1]);
+              o[4 * j + r] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb[j & 1], pt[r], o[4 * j + r], 0, 0, 0,
+                                                                             127, 0, psc[r]);
+              pin_agpr(o[4 * j + r]);
+              if (with_a) part_a(4 * j + r, key0, need_mask);
+              __builtin_amdgcn_sched_barrier(0);
             }
           }
-          float mx_raw = fmaxf(s0[0], s1[0]);
-#pragma unroll
-          for (int i = 1; i < 16; ++i) mx_raw = fmaxf(mx_raw, fmaxf(s0[i], s1[i]));
-          const float mx = mx_raw * p.s_scale_log2;  // lane max, log2 units
-          const float rm = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          m_seen = fmaxf(m_seen, rm);
-          if (m_ref == -INFINITY) m_ref = rm;
-          ovf = ovf || (rm > m_ref + kTau);
-          const float mref = m_ref > -INFINITY ? m_ref : 0.f;
-          // power-of-two block scale per query row: the row's largest p of this tile lands in
-          // (128, 256].  The MFMA's 32-element scale blocks of a column interleave both lane
-          // halves (bytes 0-15 of lanes n and n+32 take lane n's scale, bytes 16-31 take lane
-          // n+32's), so both halves of a row must carry the same scale.
-          int e = 0;
-          if (rm > -INFINITY) e = 8 - (int)ceilf(rm - mref);
-          e = min(max(e, -120), 120);
-          const float off = mref - (float)e;
-          float lsum = 0.f;
-          int pk[8];
-#pragma unroll
-          for (int w4 = 0; w4 < 8; ++w4) {
-            const v16f& sx = (w4 < 4) ? s0 : s1;
-            float pv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[4 * (w4 & 3) + j], p.s_scale_log2, -off));
-              lsum += pv[j];
-            }
-            int wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
-            wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], wv, true);
-            pk[w4] = wv;
+        };
+        auto stage = [&](int t) -> const lds_t* { return smem + (t % kStages) * kStageBytes; };
+        // The segment's last tile was loaded whole: rows past its last key hold
+        // whatever follows in the page (possibly NaN).  Their scores are masked,
+        // but 0 * NaN would still reach O through the PV MFMA, so zero them.
+        auto zero_tail = [&](int t) {
+          const int nvalid = k1 - (k0 + t * TILE);
+          if (nvalid < TILE) {
+            lds_t* z = smem + (t % kStages) * kStageBytes + nvalid * RB;
+            const int nchunks = (TILE - nvalid) * (RB / 16);
+            for (int i = 64 * wave + lane; i < nchunks; i += kThreads) *(lds_v4i*)(z + 16 * i) = v4i{0, 0, 0, 0};
+            lds_barrier();
           }
-          l_acc += __builtin_ldexpf(lsum, -e);
-          const v8i pt = v8i{pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]};
-          const int pscale = 127 - e;
-          // ---- O^T += V^T P^T over 16 blocks of 32 latent dims ----
-          auto vread = [&](int db) -> v8i {
-            const int base = vaddr[db & 1] + 64 * (db >> 1);
-            const v2i r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(st + base));
-            const v2i r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(st + base + 16 * RB));
-            const v2i r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(st + base + 32 * RB));
-            const v2i r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(st + base + 48 * RB));
-            return v8i{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-          };
-          __builtin_amdgcn_sched_barrier(0);
-          v8i vt = vread(0);
+        };
+
+        // Every wave takes part in every tile: rows past H_eff score against
+        // zero queries and are never stored.
+        issue_tile(0);
+        issue_tile(1);  // a dummy tile when the segment has one tile
+        wait_vm_barrier<kDmaPerWave>();  // tile 0 has landed
+        if (ntiles == 1) zero_tail(0);
+        dma_setup(2);
+        qk_chain(stage(0), false);
+        {
+          const bool nm = k0 + TILE > lim_min;
 #pragma unroll
-          for (int db = 0; db < 16; ++db) {
-            v8i vn = vt;
-            if (db + 1 < 16) vn = vread(db + 1);
-            o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vt, pt, o[db], 0, 0, 0, 127, 0, pscale);
-            __builtin_amdgcn_sched_barrier(0);
-            vt = vn;
-          }
-        } else {
-          // ---- bf16: S^T for one 32-key block, K = 576 in 36 steps of 16 ----
-          auto kread = [&](int c) -> v4i { return *(const lds_v4i*)(st + kaddr[c & 3] + 128 * (c >> 2)); };
-          v16f s0 = v16f{0};
-          v4i a = kread(0);
+          for (int slot = 0; slot < 16; ++slot) part_a(slot, k0, nm);
+        }
+        for (int t = 1; t < ntiles; ++t) {
+          wait_vm_barrier<kDmaPerWave>();  // tile t has landed; every wave is done with iteration t-1
+          if (t == ntiles - 1) zero_tail(t);
+          dma_setup(t + 2);
+          hb = s1;
+          qk_chain(stage(t), true);  // also finishes the softmax of tile t-1
+          p_publish();
+          lds_barrier();  // P of tile t-1 from all waves is visible
+          const int key0 = k0 + t * TILE;
+          pv_chain(stage(t - 1), true, key0, key0 + TILE > lim_min);
+        }
+        hb = s1;
+#pragma unroll
+        for (int slot = 0; slot < 17; ++slot) part_b(slot);
+        p_publish();
+        lds_barrier();
+        pv_chain(stage(ntiles - 1), false, 0, false);
+        // the dummy loads of the last two iterations must land before LDS is reused
+        wait_vm_barrier<0>();
+      } else {
+        // ---------------- bf16: 32-key tiles, one 32x32 score block ----------------
+        issue_tile(0);
+        if (1 < ntiles) issue_tile(1);
+        auto kread = [&](const lds_t* st, int c) -> v4i { return *(const lds_v4i*)(st + kaddr[c & 3] + 128 * (c >> 2)); };
+        auto vread = [&](const lds_t* st, int db, int u) -> v4i {
+          const int x = db & 1;
+          const int base0 = vaddr[x] + 128 * (db >> 1) + 16 * RB * u;
+          const int base1 = vaddr[2 + x] + 128 * (db >> 1) + 16 * RB * u;
+          const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(st + base0));
+          const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(st + base1));
+          const v2i r0i = __builtin_bit_cast(v2i, r0), r1i = __builtin_bit_cast(v2i, r1);
+          return v4i{r0i[0], r0i[1], r1i[0], r1i[1]};
+        };
+        auto qk = [&](const lds_t* st, v16f& s) {
+          s = v16f{0};
+          v4i a = kread(st, 0);
 #pragma unroll
           for (int c = 0; c < 36; ++c) {
             v4i an = a;
-            if (c + 1 < 36) an = kread(c + 1);
+            if (c + 1 < 36) an = kread(st, c + 1);
             const v4i qb = v4i{qreg[c][0], qreg[c][1], qreg[c][2], qreg[c][3]};
-            qk_mfma_bf16(s0, a, qb);
+            qk_mfma_bf16(s, a, qb, c == 35);
             __builtin_amdgcn_sched_barrier(0);
             a = an;
           }
-          qk_fence(s0);
-          if (need_mask) {
+        };
+        float mx_raw = -INFINITY, mref = 0.f, lsum = 0.f;
+        float pvv[16];
+        v4i pb[2];
+        v16f sc;
+        auto sm_chunk = [&](int i, int key0, bool need_mask) {
+          if (i == 0) {
+            mx_raw = -INFINITY;
+            lsum = 0.f;
+            if (need_mask) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = key0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-              if (key >= lim) s0[i] = -INFINITY;
+              for (int r = 0; r < 16; ++r) {
+                const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                if (key >= lim) sc[r] = -INFINITY;
+              }
             }
-          }
-          float mx_raw = s0[0];
 #pragma unroll
-          for (int i = 1; i < 16; ++i) mx_raw = fmaxf(mx_raw, s0[i]);
-          const float mx = mx_raw * p.s_scale_log2;
-          const float rm = fmaxf(mx, __shfl_xor(mx, 32, 64));
-          m_seen = fmaxf(m_seen, rm);
-          if (m_ref == -INFINITY) m_ref = rm;
-          ovf = ovf || (rm > m_ref + kTau);
-          const float mref = m_ref > -INFINITY ? m_ref : 0.f;
-          float pv[16];
-          float lsum = 0.f;
+            for (int r = 0; r < 16; ++r) mx_raw = fmaxf(mx_raw, sc[r]);
+          } else if (i == 1) {
+            const float mx = mx_raw * p.s_scale_log2;
+            const float rm = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            m_seen = fmaxf(m_seen, rm);
+            if (m_ref == -INFINITY) m_ref = rm;
+            ovf = ovf || (rm > m_ref + kTau);
+            mref = m_ref > -INFINITY ? m_ref : 0.f;
+          } else if (i >= 2 && i < 6) {
+            const int g4 = i - 2;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], p.s_scale_log2, -mref));
-            lsum += pv[i];
+            for (int j = 0; j < 4; ++j) {
+              pvv[4 * g4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * g4 + j], p.s_scale_log2, -mref));
+              lsum += pvv[4 * g4 + j];
+            }
+          } else if (i == 6 || i == 7) {
+            const int u = i - 6;
+            pb[u] = v4i{(int)pack_bf16x2(pvv[8 * u + 0], pvv[8 * u + 1]), (int)pack_bf16x2(pvv[8 * u + 2], pvv[8 * u + 3]),
+                        (int)pack_bf16x2(pvv[8 * u + 4], pvv[8 * u + 5]), (int)pack_bf16x2(pvv[8 * u + 6], pvv[8 * u + 7])};
+            if (u == 1) l_acc += lsum;
           }
-          l_acc += lsum;
-          v8bf pbf[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const v4i pb = v4i{(int)pack_bf16x2(pv[8 * u + 0], pv[8 * u + 1]), (int)pack_bf16x2(pv[8 * u + 2], pv[8 * u + 3]),
-                               (int)pack_bf16x2(pv[8 * u + 4], pv[8 * u + 5]), (int)pack_bf16x2(pv[8 * u + 6], pv[8 * u + 7])};
-            pbf[u] = __builtin_bit_cast(v8bf, pb);
-          }
-          auto vread = [&](int db, int u) -> v4i {
-            const int x = db & 1;
-            const int base0 = vaddr[x] + 128 * (db >> 1) + 16 * RB * u;
-            const int base1 = vaddr[2 + x] + 128 * (db >> 1) + 16 * RB * u;
-            const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(st + base0));
-            const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(st + base1));
-            const v2i r0i = __builtin_bit_cast(v2i, r0), r1i = __builtin_bit_cast(v2i, r1);
-            return v4i{r0i[0], r0i[1], r1i[0], r1i[1]};
-          };
-          __builtin_amdgcn_sched_barrier(0);
-          v4i vt0 = vread(0, 0), vt1 = vread(0, 1);
+        };
+        auto pv = [&](const lds_t* st, const v4i& p0, const v4i& p1, bool with_sm, int key0, bool need_mask) {
+          const v8bf pbf0 = __builtin_bit_cast(v8bf, p0), pbf1 = __builtin_bit_cast(v8bf, p1);
+          v4i vt0 = vread(st, 0, 0), vt1 = vread(st, 0, 1);
 #pragma unroll
           for (int db = 0; db < 16; ++db) {
             v4i vn0 = vt0, vn1 = vt1;
             if (db + 1 < 16) {
-              vn0 = vread(db + 1, 0);
-              vn1 = vread(db + 1, 1);
+              vn0 = vread(st, db + 1, 0);
+              vn1 = vread(st, db + 1, 1);
             }
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, vt0), pbf[0], o[db], 0, 0, 0);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, vt1), pbf[1], o[db], 0, 0, 0);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, vt0), pbf0, o[db], 0, 0, 0);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, vt1), pbf1, o[db], 0, 0, 0);
+            if (with_sm && db < 8) sm_chunk(db, key0, need_mask);
             __builtin_amdgcn_sched_barrier(0);
             vt0 = vn0;
             vt1 = vn1;
           }
+        };
+
+        wait_tile_barrier(min(1, ntiles - 1));
+        if (2 < ntiles) issue_tile(2);
+        v4i pp0 = v4i{0, 0, 0, 0}, pp1 = v4i{0, 0, 0, 0};
+        if (wave_active) {
+          qk(smem, sc);
+          const bool nm = k0 + TILE > lim_min;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sm_chunk(i, k0, nm);
+          pp0 = pb[0];
+          pp1 = pb[1];
         }
+        for (int tt = 1; tt < ntiles; ++tt) {
+          wait_tile_barrier(min(1, ntiles - 1 - tt));
+          if (tt + 2 < ntiles) issue_tile(tt + 2);
+          if (!wave_active) continue;
+          const lds_t* st = smem + (tt % kStages) * kStageBytes;
+          const lds_t* stp = smem + ((tt - 1) % kStages) * kStageBytes;
+          const int key0 = k0 + tt * TILE;
+          qk(st, sc);
+          pv(stp, pp0, pp1, true, key0, key0 + TILE > lim_min);
+          pp0 = pb[0];
+          pp1 = pb[1];
+        }
+        if (wave_active) pv(smem + ((ntiles - 1) % kStages) * kStageBytes, pp0, pp1, false, 0, false);
       }
       // did any row of the workgroup outgrow its reference?
       const bool wave_ovf = __builtin_amdgcn_ballot_w64(ovf) != 0;
@@ -542,92 +819,188 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   }
 
   // ---- epilogue: normalise, write final or partial ----
-  // The 32x512 accumulator tile of each wave goes through LDS in four
-  // 128-column passes (stored straight from the accumulator registers), then
-  // every lane writes 64 contiguous columns of one row.
-  const float l_tot = l_acc + __shfl_xor(l_acc, 32, 64);
+  if constexpr (DT == kFp8) {
+    // Wave w holds O^T for latent dims [128w, 128w+128) of all 128 rows; the
+    // row owners publish 1/l, then the whole 128x512 tile is staged in LDS and
+    // written row-contiguous (whole 128-byte lines per store).
+    asm volatile("" : "+v"(lane));
+    const int ne = lane & 31, he = lane >> 5;
+    const float l_tot = xor32_sum(l_acc);
+    const bool has = l_tot > 0.f;
+    const float inv = has ? p.v_scale / l_tot : 0.f;
+    const float lse_v = has ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    typedef __attribute__((address_space(3))) float lds_f32;
+    lds_f32* s_inv = (lds_f32*)(smem + kPOffset);
+    lds_barrier();  // every wave is done with the KV ring and the P buffer
+    if (he == 0) s_inv[32 * wave + ne] = inv;
+    lds_barrier();
+    float invr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) invr[r] = s_inv[32 * r + ne];
+    const bool f32out = !sg.single && !p.part_bf16;
+    const int row0 = mt * kTileM;
+    if (!f32out) {
+      uint16_t* dst = sg.single ? p.out + (size_t)sg.b * rows_per_b * kDv
+                                : (uint16_t*)p.part_o + (size_t)sg.slot * rows_per_b * kDv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int row = 32 * r + ne, col = 128 * wave + 32 * j + 8 * gq + 4 * he;
+            const v16f& acc = o[4 * j + r];
+            const v2i w = v2i{(int)pack_bf16x2(acc[4 * gq + 0] * invr[r], acc[4 * gq + 1] * invr[r]),
+                              (int)pack_bf16x2(acc[4 * gq + 2] * invr[r], acc[4 * gq + 3] * invr[r])};
+            *(lds_v2i*)(smem + row * kEpiPitch + 2 * col) = w;
+          }
+        }
+      }
+      lds_barrier();
+#pragma unroll 4
+      for (int k = 0; k < 32; ++k) {
+        const int row = 32 * wave + k;
+        const v4i v = *(const lds_v4i*)(smem + row * kEpiPitch + 16 * lane);
+        const int m_r = row0 + row;
+        if (m_r < p.H_eff) {
+          const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
+          *(v4i*)(dst + rowb * kDv + 8 * lane) = v;
+        }
+      }
+    } else {
+      float* dst = (float*)p.part_o + (size_t)sg.slot * rows_per_b * kDv;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if ((wave >> 1) == h) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+#pragma unroll
+              for (int gq = 0; gq < 4; ++gq) {
+                const int row = 32 * r + ne, col = 128 * (wave & 1) + 32 * j + 8 * gq + 4 * he;
+                const v16f& acc = o[4 * j + r];
+                *(__attribute__((address_space(3))) v4f*)(smem + row * kEpiPitch + 4 * col) =
+                    v4f{acc[4 * gq + 0] * invr[r], acc[4 * gq + 1] * invr[r], acc[4 * gq + 2] * invr[r],
+                        acc[4 * gq + 3] * invr[r]};
+              }
+            }
+          }
+        }
+        lds_barrier();
+#pragma unroll 4
+        for (int k = 0; k < 32; ++k) {
+          const int row = 32 * wave + k;
+          const v4f v = *(const __attribute__((address_space(3))) v4f*)(smem + row * kEpiPitch + 16 * lane);
+          const int m_r = row0 + row;
+          if (m_r < p.H_eff) {
+            const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
+            *(v4f*)(dst + rowb * kDv + 256 * h + 4 * lane) = v;
+          }
+        }
+        lds_barrier();
+      }
+    }
+    const int m_l = row0 + 32 * wave + ne;
+    if (m_l < p.H_eff && he == 0) {
+      const size_t rowb = (size_t)gF * p.H + (size_t)m_l;
+      if (sg.single) {
+        if (p.lse != nullptr) p.lse[(size_t)sg.b * rows_per_b + rowb] = lse_v;
+      } else {
+        p.part_lse[(size_t)sg.slot * rows_per_b + rowb] = lse_v;
+      }
+    }
+  } else {
+  // Each wave moves its 32x512 tile through its own LDS region in two passes
+  // of 256 columns: accumulators are scaled by 1/l and converted to the
+  // output type on the way in (rows padded so the column-wise writes hit
+  // distinct banks), then read back row-contiguous so that every store
+  // instruction writes whole 128-byte lines.
+  asm volatile("" : "+v"(lane));  // epilogue addressing is computed here, after the loop
+  const int ne = lane & 31, he = lane >> 5;
+  const float l_tot = xor32_sum(l_acc);
   const bool has = l_tot > 0.f;
   const float inv = has ? p.v_scale / l_tot : 0.f;
   const float lse_v = has ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
-  const int rr = lane >> 1, hf = lane & 1;  // read-back role: row rr, columns [64*hf, +64) of the pass
-  const float inv_r = __shfl(inv, rr, 64);
-  const float lse_r = __shfl(lse_v, rr, 64);
-  const int m_r = mt * kTileM + 32 * wave + rr;
-  const bool valid_r = m_r < p.H_eff;
-  const size_t rowb_r = (size_t)gF * p.H + (size_t)m_r;
+  const bool f32out = !sg.single && !p.part_bf16;
+  const int wrow0 = mt * kTileM + 32 * wave;  // first row of this wave
   lds_barrier();  // every wave is done with the KV ring
-  lds_t* wl = smem + wave * 16384;
+  lds_t* wl = smem + wave * kEpiWaveBytes;
+  if (!f32out) {
+    uint16_t* dst = sg.single ? p.out + (size_t)sg.b * rows_per_b * kDv
+                              : (uint16_t*)p.part_o + (size_t)sg.slot * rows_per_b * kDv;
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
+    for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int dbl = 0; dbl < 4; ++dbl) {
-      const int db = 4 * pass + dbl;
+      for (int dbl = 0; dbl < 8; ++dbl) {
+        const int db = 8 * pass + dbl;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int dl = 32 * dbl + 8 * i + 4 * hh;
-        *(__attribute__((address_space(3))) v4f*)(wl + (n * 128 + dl) * 4) =
-            v4f{o[db][4 * i + 0], o[db][4 * i + 1], o[db][4 * i + 2], o[db][4 * i + 3]};
+        for (int i = 0; i < 4; ++i) {
+          const int col = 32 * dbl + 8 * i + 4 * he;
+          const v2i w = v2i{(int)pack_bf16x2(o[db][4 * i + 0] * inv, o[db][4 * i + 1] * inv),
+                            (int)pack_bf16x2(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv)};
+          *(lds_v2i*)(wl + ne * kEpiRowB16 + 2 * col) = w;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int r = 2 * k + (lane >> 5), ch = lane & 31;
+        const v4i v = *(const lds_v4i*)(wl + r * kEpiRowB16 + 16 * ch);
+        const int m_r = wrow0 + r;
+        if (m_r < p.H_eff) {
+          const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
+          *(v4i*)(dst + rowb * kDv + 256 * pass + 8 * ch) = v;
+        }
       }
     }
-    float v[64];
+  } else {
+    float* dst = (float*)p.part_o + (size_t)sg.slot * rows_per_b * kDv;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const v4f x = *(const __attribute__((address_space(3))) v4f*)(wl + (rr * 128 + 64 * hf + 4 * k) * 4);
-      v[4 * k + 0] = x[0] * inv_r;
-      v[4 * k + 1] = x[1] * inv_r;
-      v[4 * k + 2] = x[2] * inv_r;
-      v[4 * k + 3] = x[3] * inv_r;
-    }
-    if (valid_r) {
-      const int d0 = 128 * pass + 64 * hf;
-      if (sg.single) {
-        uint16_t* orow = p.out + ((size_t)sg.b * rows_per_b + rowb_r) * kDv + d0;
+    for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          uint4 w;
-          w.x = pack_bf16x2(v[8 * k + 0], v[8 * k + 1]);
-          w.y = pack_bf16x2(v[8 * k + 2], v[8 * k + 3]);
-          w.z = pack_bf16x2(v[8 * k + 4], v[8 * k + 5]);
-          w.w = pack_bf16x2(v[8 * k + 6], v[8 * k + 7]);
-          *(uint4*)(orow + 8 * k) = w;
+      for (int dbl = 0; dbl < 8; ++dbl) {
+        const int db = 8 * pass + dbl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = 32 * dbl + 8 * i + 4 * he;
+          *(__attribute__((address_space(3))) v4f*)(wl + ne * kEpiRowF32 + 4 * col) =
+              v4f{o[db][4 * i + 0] * inv, o[db][4 * i + 1] * inv, o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv};
         }
-      } else if (p.part_bf16) {
-        uint16_t* orow = (uint16_t*)p.part_o + ((size_t)sg.slot * rows_per_b + rowb_r) * kDv + d0;
+      }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          uint4 w;
-          w.x = pack_bf16x2(v[8 * k + 0], v[8 * k + 1]);
-          w.y = pack_bf16x2(v[8 * k + 2], v[8 * k + 3]);
-          w.z = pack_bf16x2(v[8 * k + 4], v[8 * k + 5]);
-          w.w = pack_bf16x2(v[8 * k + 6], v[8 * k + 7]);
-          *(uint4*)(orow + 8 * k) = w;
+      for (int r = 0; r < 32; ++r) {
+        const v4f v = *(const __attribute__((address_space(3))) v4f*)(wl + r * kEpiRowF32 + 16 * lane);
+        const int m_r = wrow0 + r;
+        if (m_r < p.H_eff) {
+          const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
+          *(v4f*)(dst + rowb * kDv + 256 * pass + 4 * lane) = v;
         }
-      } else {
-        float* orow = (float*)p.part_o + ((size_t)sg.slot * rows_per_b + rowb_r) * kDv + d0;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) *(v4f*)(orow + 4 * k) = v4f{v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]};
       }
     }
   }
-  if (valid_r && hf == 0) {
+  const int m_l = wrow0 + ne;
+  if (m_l < p.H_eff && he == 0) {
+    const size_t rowb = (size_t)gF * p.H + (size_t)m_l;
     if (sg.single) {
-      if (p.lse != nullptr) p.lse[(size_t)sg.b * rows_per_b + rowb_r] = lse_r;
+      if (p.lse != nullptr) p.lse[(size_t)sg.b * rows_per_b + rowb] = lse_v;
     } else {
-      p.part_lse[(size_t)sg.slot * rows_per_b + rowb_r] = lse_r;
+      p.part_lse[(size_t)sg.slot * rows_per_b + rowb] = lse_v;
     }
+  }
   }
 }
 
 template <int DT, bool FAST>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_split_kv_partial(PartialParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kLdsBytes];
   __shared__ long long s_red[4];
   __shared__ long long s_found[2];
   __shared__ int s_flag[4];
   lds_t* smem = (lds_t*)smem_raw;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases in SGPRs
   int w, u;
   if (p.xcd_map) {
     // the U workgroups of one slice are consecutive dispatches of one XCD
@@ -709,62 +1082,87 @@ mla_split_kv_partial(PartialParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge: one wave per output row.
+// Merge: one workgroup per output row.  The slice weights exp(lse_s - LSE)
+// are computed once per row into LDS (256 slices at a time); each of the four
+// waves then sums 128 of the 512 latent columns (two per lane), with sixteen
+// slices' loads in flight.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) mla_combine(CombineParams p) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long long grow = (long long)blockIdx.x * 4 + wave;
+  __shared__ float s_w[256];
+  __shared__ float s_red[4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const long long grow = (long long)blockIdx.x;
   if (grow >= (long long)p.B * p.rows_per_b) return;
   const int b = (int)(grow / p.rows_per_b);
   const int row = (int)(grow - (long long)b * p.rows_per_b);
   const int w0 = max(p.meta[2 * b], 0), w1 = min(p.meta[2 * b + 1], p.G - 1);
   if (w0 >= w1) return;  // single slice: written by the partial kernel
-  // slices of the range that hold no work (more slices than units) wrote nothing
+  // slices that hold no work (more slices than units) wrote nothing: weight 0
   const long long T = *(const long long*)(p.meta + 2 * p.B);
-  auto empty = [&](int s) { return slice_start(s, T, p.G) == slice_start(s + 1, T, p.G); };
-
+  auto lse_of = [&](int s) -> float {
+    if (slice_start(s, T, p.G) == slice_start(s + 1, T, p.G)) return -INFINITY;
+    return p.part_lse[(size_t)(s + b) * p.rows_per_b + row];
+  };
+  const int n = w1 - w0 + 1;
+  // LSE over the slices (each thread keeps the lse values of its slices)
+  float my[4];
   float mx = -INFINITY;
-  for (int s = w0 + lane; s <= w1; s += 64)
-    if (!empty(s)) mx = fmaxf(mx, p.part_lse[(size_t)(s + b) * p.rows_per_b + row]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + 256 * k;
+    my[k] = i < n ? lse_of(w0 + i) : -INFINITY;
+    mx = fmaxf(mx, my[k]);
+  }
+  for (int i = tid + 1024; i < n; i += 256) mx = fmaxf(mx, lse_of(w0 + i));
   mx = wave_max(mx);
-  float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float lse_out = -INFINITY;
+  if (lane == 0) s_red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  __syncthreads();
+  float sum = 0.f;
   if (mx > -INFINITY) {
-    float sum = 0.f;
-    for (int s = w0 + lane; s <= w1; s += 64)
-      if (!empty(s)) sum += expf(p.part_lse[(size_t)(s + b) * p.rows_per_b + row] - mx);
-    sum = wave_sum(sum);
-    lse_out = mx + logf(sum);
-    for (int s = w0; s <= w1; ++s) {
-      if (empty(s)) continue;
-      const size_t prow = (size_t)(s + b) * p.rows_per_b + row;
-      const float wgt = expf(p.part_lse[prow] - lse_out);
-      if (p.part_bf16) {
-        const uint4 x = *(const uint4*)((const uint16_t*)p.part_o + prow * kDv + 8 * lane);
-        const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[2 * j] += wgt * __builtin_bit_cast(float, xs[j] << 16);
-          v[2 * j + 1] += wgt * __builtin_bit_cast(float, xs[j] & 0xffff0000u);
-        }
-      } else {
-        const v4f* src = (const v4f*)((const float*)p.part_o + prow * kDv + 8 * lane);
-        const v4f x0 = src[0], x1 = src[1];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[j] += wgt * x0[j];
-          v[4 + j] += wgt * x1[j];
-        }
+    for (int k = 0; k < 4; ++k) sum += expf(my[k] - mx);
+    for (int i = tid + 1024; i < n; i += 256) sum += expf(lse_of(w0 + i) - mx);
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) s_red[wave] = sum;
+  __syncthreads();
+  sum = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+  const float lse_out = mx > -INFINITY ? mx + logf(sum) : -INFINITY;
+
+  const int d = 128 * wave + 2 * lane;
+  float acc0 = 0.f, acc1 = 0.f;
+  const size_t st_rows = (size_t)p.rows_per_b * kDv;  // elements between consecutive slots
+  const size_t base = ((size_t)(w0 + b) * p.rows_per_b + row) * kDv + d;
+  for (int c0 = 0; c0 < n && mx > -INFINITY; c0 += 256) {
+    const int cn = min(256, n - c0);
+    __syncthreads();
+    if (tid < cn) s_w[tid] = expf((c0 + tid < 1024 ? my[(c0 + tid) >> 8] : lse_of(w0 + c0 + tid)) - lse_out);
+    __syncthreads();
+    if (p.part_bf16) {
+      const uint16_t* src = (const uint16_t*)p.part_o + base + (size_t)c0 * st_rows;
+#pragma unroll 16
+      for (int i = 0; i < cn; ++i) {
+        const float wgt = s_w[i];
+        const uint32_t x = *(const uint32_t*)(src + (size_t)i * st_rows);
+        // slots of empty slices hold stale bytes: select, never multiply them by 0
+        acc0 += wgt > 0.f ? wgt * __builtin_bit_cast(float, x << 16) : 0.f;
+        acc1 += wgt > 0.f ? wgt * __builtin_bit_cast(float, x & 0xffff0000u) : 0.f;
+      }
+    } else {
+      const float* src = (const float*)p.part_o + base + (size_t)c0 * st_rows;
+#pragma unroll 16
+      for (int i = 0; i < cn; ++i) {
+        const float wgt = s_w[i];
+        const float2 x = *(const float2*)(src + (size_t)i * st_rows);
+        acc0 += wgt > 0.f ? wgt * x.x : 0.f;
+        acc1 += wgt > 0.f ? wgt * x.y : 0.f;
       }
     }
   }
-  uint4 w;
-  w.x = pack_bf16x2(v[0], v[1]);
-  w.y = pack_bf16x2(v[2], v[3]);
-  w.z = pack_bf16x2(v[4], v[5]);
-  w.w = pack_bf16x2(v[6], v[7]);
-  *(uint4*)(p.out + ((size_t)b * p.rows_per_b + row) * kDv + 8 * lane) = w;
-  if (p.lse != nullptr && lane == 0) p.lse[(size_t)b * p.rows_per_b + row] = lse_out;
+  *(uint32_t*)(p.out + ((size_t)b * p.rows_per_b + row) * kDv + d) = pack_bf16x2(acc0, acc1);
+  if (p.lse != nullptr && tid == 0) p.lse[(size_t)b * p.rows_per_b + row] = lse_out;
 }
 
 // ---------------------------------------------------------------------------
@@ -833,7 +1231,7 @@ hipError_t launch_partial(const PartialParams& p, int dtype, bool fast_pages, hi
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   const long long rows = (long long)p.B * p.rows_per_b;
-  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  const dim3 grid((unsigned)rows), block(256);
   hipLaunchKernelGGL(mla_combine, grid, block, 0, stream, p);
   return hipGetLastError();
 }

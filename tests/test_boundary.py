@@ -54,7 +54,7 @@ def test_plan_fold_factor_and_workspace(B, q_len, H, L, F):
     if ns > 1:
         assert ns < 8 or ns % 8 == 0  # equal share per XCD once there are enough slices
         rows = q_len * H
-        need = (ns + B) * rows * (512 * 4 + 4) + B * 8 + 8
+        need = (ns + B) * rows * (512 * 2 + 4) + B * 8 + 8  # bf16 partials by default
         assert need <= ws <= need + 3 * 256
     else:
         assert ws == 0
@@ -68,10 +68,10 @@ def test_plan_tiny_shape_needs_no_merge():
 
 
 def test_plan_options():
-    ns, fold, ws = mla.plan_for_cus(4, 4, 32, 81920, 256, mla.options(num_splits=24, partial_bf16=True, no_fold=True))
+    ns, fold, ws = mla.plan_for_cus(4, 4, 32, 81920, 256, mla.options(num_splits=24, partial_fp32=True, no_fold=True))
     assert ns == 24 and fold == 1
     rows = 4 * 32
-    assert ws >= (24 + 4) * rows * (512 * 2 + 4)
+    assert ws >= (24 + 4) * rows * (512 * 4 + 4)
 
 
 def test_plan_rejects_bad_sizes():

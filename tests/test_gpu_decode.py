@@ -58,10 +58,10 @@ def test_fold_and_partial_precision_options(dtype):
     ref = run_oracle(x)
     base, lse_b = run_gpu(x)
     nofold, lse_n = run_gpu(x, opts=mla.options(no_fold=True))
-    pb16, lse_p = run_gpu(x, opts=mla.options(partial_bf16=True, num_splits=16))
+    pf32, lse_p = run_gpu(x, opts=mla.options(partial_fp32=True, num_splits=16))
     assert_parity(x, base, lse_b, ref)
     assert_parity(x, nofold, lse_n, ref)
-    assert_parity(x, pb16, lse_p, ref, partial_bf16=True)
+    assert_parity(x, pf32, lse_p, ref, partial_fp32=True)
     # folding only re-indexes rows: identical per-row arithmetic
     assert torch.equal(base, nofold) and torch.equal(lse_b, lse_n)
 
