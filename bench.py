@@ -73,6 +73,156 @@ def load_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling the rocprofv3 byte counters.
+
+    Run under `rocprofv3 --pmc FETCH_SIZE` (and separately WRITE_SIZE): each of
+    the three launches reads COPY_BYTES and writes COPY_BYTES.
+    """
+    import torch
+
+    x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.add(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    print(f"copy calibration: {COPY_BYTES} bytes read and {COPY_BYTES} bytes written per launch", flush=True)
+
+
+def _csv_rows(path):
+    import csv
+    import glob
+
+    files = sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)) or \
+        sorted(glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no rocprofv3 csv under {path}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_avg(path, counter, name_part):
+    """Mean per-dispatch value (KiB, as rocprofv3 reports it) of `counter` for kernels matching name_part."""
+    vals = [float(r["Counter_Value"]) for r in _csv_rows(path)
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"{counter} for {name_part!r} not found under {path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def _trace_regions(path):
+    """Per-region kernel timings from the dispatch trace of one bench.py run, in the order bench.py runs
+    them: steps (split-KV then merge), split-KV alone back to back, merge alone back to back."""
+    import csv
+    import glob
+    import re
+
+    files = sorted(glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        return {}
+    with open(files[0]) as f:
+        ev = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                     "P" if "split_kv_partial" in r["Kernel_Name"] else "M" if "combine" in r["Kernel_Name"] else "o")
+                    for r in csv.DictReader(f))
+    seq = "".join(e[2] for e in ev)
+    out = {}
+
+    def stats(idx, stride):
+        dur = [(ev[i][1] - ev[i][0]) / 1e3 for i in idx]
+        per = [(ev[j][0] - ev[i][0]) / 1e3 for i, j in zip(idx[:-1], idx[1:])]
+        return round(sum(dur) / len(dur), 2), round(sum(per) / len(per), 2) if per else None
+
+    m = re.search(r"(?:PM){5,}", seq)  # the timed steps (the first run of them)
+    if m:
+        ps = list(range(m.start(), m.end(), 2))
+        d_p, period = stats(ps, 2)
+        d_m, _ = stats([i + 1 for i in ps], 2)
+        out["steps"] = {"split_kv_us": d_p, "merge_us": d_m, "step_period_us": period}
+    m = re.search(r"P{5,}", seq)
+    if m:
+        d_p, period = stats(list(range(m.start(), m.end())), 1)
+        out["split_kv_alone"] = {"duration_us": d_p, "period_us": period}
+    m = re.search(r"M{5,}", seq)
+    if m:
+        d_m, period = stats(list(range(m.start(), m.end())), 1)
+        out["merge_alone"] = {"duration_us": d_m, "period_us": period}
+    return out
+
+
+def summarize_profile(d: str, workload: str):
+    """Turn the rocprofv3 runs under d/ (trace, fetch, write, cal_fetch, cal_write) into
+    profiles/<kernel>_<workload>.md and the traffic JSON bench.py reports."""
+    stats = _csv_rows(os.path.join(d, "trace"))
+    cal_f, _ = _counter_avg(os.path.join(d, "cal_fetch"), "FETCH_SIZE", "CUDAFunctorOnSelf_add")
+    cal_w, _ = _counter_avg(os.path.join(d, "cal_write"), "WRITE_SIZE", "CUDAFunctorOnSelf_add")
+    f_scale = COPY_BYTES / (cal_f * 1024.0)
+    w_scale = COPY_BYTES / (cal_w * 1024.0)
+    out = {"workload": workload, "kernel_source_sha256_16": kernel_hash(),
+           "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": cal_f, "write_kib": cal_w,
+                           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+           "kernels": {}}
+    for short, part in (("mla_split_kv_partial", "mla_split_kv_partial"), ("mla_combine", "mla_combine")):
+        fk, nf = _counter_avg(os.path.join(d, "fetch"), "FETCH_SIZE", part)
+        wk, nw = _counter_avg(os.path.join(d, "write"), "WRITE_SIZE", part)
+        st = [r for r in stats if part in r["Name"]]
+        avg_ns = float(st[0]["AverageNs"]) if st else None
+        out["kernels"][short] = {"fetch_bytes": round(fk * 1024 * f_scale), "write_bytes": round(wk * 1024 * w_scale),
+                                 "dispatches_counted": [nf, nw], "avg_duration_ns": avg_ns,
+                                 "calls": int(st[0]["Calls"]) if st else None}
+    kp = out["kernels"]["mla_split_kv_partial"]
+    out["hbm_bytes_per_launch"] = kp["fetch_bytes"] + kp["write_bytes"]
+    out["regions"] = _trace_regions(os.path.join(d, "trace"))
+    base = os.path.join(ROOT, "profiles")
+    with open(os.path.join(base, f"mla_split_kv_partial_{workload}_traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    lines = [f"# rocprofv3 summary: {workload}", "",
+             "Kernel trace (`--kernel-trace --stats`) of one `bench.py --steps 20 --warmup 5` run: the warm-up, the "
+             "timed steps, each kernel alone, and two replays of the captured graph:", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| {r['Name'][:70]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    reg = out["regions"]
+    if reg:
+        lines += ["", "The same trace by region of the bench run (durations are kernel execution; periods are "
+                  "start-to-start, so they include the dispatch gaps bench.py's events also see):", ""]
+        if "steps" in reg:
+            r = reg["steps"]
+            lines.append(f"- steps: split-KV {r['split_kv_us']} us, merge {r['merge_us']} us, one step every "
+                         f"{r['step_period_us']} us")
+        if "split_kv_alone" in reg:
+            r = reg["split_kv_alone"]
+            lines.append(f"- split-KV alone, back to back: {r['duration_us']} us each, one every {r['period_us']} us "
+                         "(what `kernels_ms.split_kv_partial` and `roofline.avg_launch_ms` measure)")
+        if "merge_alone" in reg:
+            r = reg["merge_alone"]
+            lines.append(f"- merge alone, back to back: {r['duration_us']} us each, one every {r['period_us']} us")
+    lines += ["", "HBM traffic per launch (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`), scaled by a copy of "
+              f"{COPY_BYTES} bytes (fetch x{f_scale:.3f}, write x{w_scale:.3f}):", "",
+              "| kernel | read MB | written MB |", "|---|---|---|"]
+    for k, v in out["kernels"].items():
+        lines.append(f"| {k} | {v['fetch_bytes'] / 1e6:.2f} | {v['write_bytes'] / 1e6:.2f} |")
+    lines += ["", f"Kernel source sha256/16: `{out['kernel_source_sha256_16']}`", "", "Commands (repository root):", "",
+              "```",
+              f"rocprofv3 --kernel-trace --stats -d {d}/trace -o run --output-format csv -- "
+              f"python3 bench.py --workload {workload} --steps 20 --warmup 5 --no-cpu-baseline",
+              f"rocprofv3 --pmc FETCH_SIZE -d {d}/fetch -o run --output-format csv -- "
+              f"python3 bench.py --workload {workload} --steps 5 --warmup 2 --no-cpu-baseline",
+              f"rocprofv3 --pmc WRITE_SIZE -d {d}/write -o run --output-format csv -- "
+              f"python3 bench.py --workload {workload} --steps 5 --warmup 2 --no-cpu-baseline",
+              f"rocprofv3 --pmc FETCH_SIZE -d {d}/cal_fetch -o run --output-format csv -- python3 bench.py --copy-calibration",
+              f"rocprofv3 --pmc WRITE_SIZE -d {d}/cal_write -o run --output-format csv -- python3 bench.py --copy-calibration",
+              f"python3 bench.py --summarize-profile {d} --workload {workload}",
+              "```", ""]
+    with open(os.path.join(base, f"mla_split_kv_partial_{workload}.md"), "w") as f:
+        f.write("\n".join(lines))
+    print(json.dumps(out))
+
+
 def cpu_baseline(x, max_threads: int):
     """Time the fp64 oracle on all (sequence, token) rows over a prefix of every sequence's keys."""
     import numpy as np
@@ -80,7 +230,7 @@ def cpu_baseline(x, max_threads: int):
     import oracle
 
     threads = max(1, min(max_threads, os.cpu_count() or 1, x.B * x.q_len))
-    frac = 0.25 if x.name.startswith("agentic") else 0.05
+    frac = 1.0 if x.name.startswith("agentic") else 0.05
     lens = np.maximum(1, (x.seq_lens.astype(np.int64) * frac).astype(np.int64)).astype(np.int32)
     oracle.mla_decode(x.q[:1, :1, :1], x.kv_cache, x.block_table[:1], np.minimum(lens[:1], 64), dtype=x.dtype,
                       softmax_scale=x.softmax_scale, q_scale=x.q_scale, kv_scale=x.kv_scale, num_threads=1)
@@ -105,7 +255,15 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--num-splits", type=int, default=0, help="override the planned KV slice count")
     ap.add_argument("--partial-fp32", action="store_true", help="keep split partials in fp32 (default bf16)")
+    ap.add_argument("--copy-calibration", action="store_true", help="run the counter-calibration copy and exit")
+    ap.add_argument("--summarize-profile", metavar="DIR", help="summarise rocprofv3 runs under DIR into profiles/")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.workload)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "sequences are independent, see DESIGN.md for how the decode would shard", file=sys.stderr)
@@ -141,40 +299,66 @@ def main():
     stream = torch.cuda.current_stream(dev)
     del x.kv_cache  # host copy no longer needed (the CPU baseline regenerates if asked)
 
-    def step(i, split_event=None):
-        opts = mla.options(num_splits=args.num_splits, partial_fp32=args.partial_fp32, split_event=split_event)
-        mla.decode(q, kvs[i % copies], bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_seq_len=x.max_seq_len,
-                   out=out, lse=lse, workspace=ws, opts=opts, stream=stream.cuda_stream)
+    calls = {}
+
+    def step(i, stages=0, st=None):
+        """Call i of a timed loop (KV copy i % copies); the arguments are marshalled once per (copy, stages,
+        stream) so the loop measures the kernels, not the Python binding."""
+        key = (i % copies, stages, (st or stream).cuda_stream)
+        if key not in calls:
+            opts = mla.options(num_splits=args.num_splits, partial_fp32=args.partial_fp32, stages=stages)
+            calls[key] = mla.PreparedDecode(q, kvs[i % copies], bt, sl, x.softmax_scale, x.q_scale, x.kv_scale,
+                                            max_seq_len=x.max_seq_len, out=out, lse=lse, workspace=ws, opts=opts,
+                                            stream=(st or stream).cuda_stream)
+        else:
+            calls[key]()
+
+    def timed_eager(stages, first):
+        """K back-to-back calls between two events on the launch stream; ms per call."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(K):
+            step(first + i, stages)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    def timed_graph(stages, first):
+        """K calls captured into one HIP graph, replayed between two events on the replay stream: the
+        kernels back to back without host launch overhead.  Returns (ms per call, wall seconds)."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream()
+            for i in range(K):
+                step(first + i, stages, st=cap)
+        torch.cuda.synchronize()
+        g.replay()  # one untimed replay
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K, time.perf_counter() - t0
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     K = args.steps
-    ev_start = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev_mid = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    for e in ev_mid:  # creates the underlying hipEvent_t
-        e.record(stream)
-    torch.cuda.synchronize()
-    t_all0 = torch.cuda.Event(enable_timing=True)
-    t_all1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_all0.record(stream)
-    for i in range(K):
-        ev_start[i].record(stream)
-        step(args.warmup + i, split_event=ev_mid[i].cuda_event)
-        ev_end[i].record(stream)
-    t_all1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_all0.elapsed_time(t_all1)
-    ms_per_step = total_ms / K
-    part_ms = [ev_start[i].elapsed_time(ev_mid[i]) for i in range(K)]
-    merge_ms = [ev_mid[i].elapsed_time(ev_end[i]) for i in range(K)]
-    step_ms = [ev_start[i].elapsed_time(ev_end[i]) for i in range(K)]
-    part_avg = sum(part_ms) / K
+    # the step: both kernels, K times back to back (the headline figure)
+    t0 = time.perf_counter()
+    ms_per_step = timed_eager(0, args.warmup)
+    wall = time.perf_counter() - t0
+    # each kernel alone, back to back, for its roofline (the merge re-merges the partials just written)
+    part_avg = timed_eager(1, args.warmup + K)
+    merge_avg = timed_eager(2, args.warmup + 2 * K) if num_splits > 1 else 0.0
+    # the same K steps captured into one HIP graph and replayed (reported beside the headline)
+    graph_ms, _ = timed_graph(0, args.warmup)
 
     value = alg["kv_bytes"] / (ms_per_step * 1e-3) / 1e12
     achieved = alg["bytes"] / (part_avg * 1e-3) / 1e9
@@ -190,6 +374,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "graph_us_per_step": round(graph_ms * 1e3, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(pages_us / (ms_per_step * 1e3), 4) if pages_us else None,
@@ -203,8 +388,7 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": alg["bytes"],
                      "avg_launch_ms": round(part_avg, 5)},
-        "kernels_ms": {"split_kv_partial": round(part_avg, 5), "merge": round(sum(merge_ms) / K, 5),
-                       "step_p10": round(sorted(step_ms)[K // 10], 5), "step_p90": round(sorted(step_ms)[(9 * K) // 10], 5)},
+        "kernels_ms": {"split_kv_partial": round(part_avg, 5), "merge": round(merge_avg, 5)},
         "tflops": round(tflops, 1),
         "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS[x.dtype], 4),
         "wall_s_timed": round(wall, 4),

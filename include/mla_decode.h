@@ -140,7 +140,10 @@ typedef struct mla_options {
   int32_t num_splits;   /* > 0: use this many KV slices instead of the planned count */
   int32_t no_fold;      /* != 0: do not fold query tokens into heads (F = 1) */
   int32_t partial_fp32; /* != 0: keep the split partial outputs in fp32 (default: bf16) */
-  int32_t reserved[5];
+  int32_t stages;       /* 0: both kernels; 1: only the split-KV kernel; 2: only the merge kernel
+                           (re-merging the partials a previous call with the same arguments left in
+                           the workspace).  1 and 2 exist to time each kernel back to back. */
+  int32_t reserved[4];
   void* split_event;    /* hipEvent_t or NULL: recorded on `stream` after the split-KV kernel
                            and before the merge kernel, so callers can time each kernel */
 } mla_options;

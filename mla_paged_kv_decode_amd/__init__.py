@@ -46,15 +46,18 @@ class MlaShape(ctypes.Structure):
 
 class MlaOptions(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int32), ("no_fold", ctypes.c_int32), ("partial_fp32", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 5), ("split_event", ctypes.c_void_p)]
+                ("stages", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4), ("split_event", ctypes.c_void_p)]
 
 
-def options(num_splits: int = 0, no_fold: bool = False, partial_fp32: bool = False, split_event=None) -> MlaOptions:
-    """mla_options; split_event is a raw hipEvent_t (e.g. torch.cuda.Event().cuda_event after one record)."""
+def options(num_splits: int = 0, no_fold: bool = False, partial_fp32: bool = False, split_event=None,
+            stages: int = 0) -> MlaOptions:
+    """mla_options; split_event is a raw hipEvent_t (e.g. torch.cuda.Event().cuda_event after one record);
+    stages 1 / 2 launch only the split-KV / only the merge kernel."""
     o = MlaOptions()
     o.num_splits = int(num_splits)
     o.no_fold = int(bool(no_fold))
     o.partial_fp32 = int(bool(partial_fp32))
+    o.stages = int(stages)
     o.split_event = split_event
     return o
 
@@ -195,6 +198,32 @@ def decode(q, kv_cache, block_table, seq_lens, softmax_scale: float, q_scale: fl
     else:
         _check(lib().mla_decode_ex(*args, ctypes.byref(opts)))
     return out, lse
+
+
+class PreparedDecode:
+    """One decode call with its arguments marshalled once (validated by a first call), so that repeated
+    launches cost a single C call.  The tensors must stay alive and unchanged in shape."""
+
+    def __init__(self, q, kv_cache, block_table, seq_lens, softmax_scale: float, q_scale: float, kv_scale: float,
+                 *, max_seq_len: int, out, lse, workspace, opts: MlaOptions | None = None, stream=None):
+        torch = _torch()
+        _check_layout(q, kv_cache, block_table, seq_lens)
+        self._keep = (q, kv_cache, block_table, seq_lens, out, lse, workspace)
+        self._shape = make_shape(q, kv_cache, block_table, max_seq_len)
+        self._opts = opts if opts is not None else options()
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        self._args = (ctypes.byref(self._shape), q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
+                      seq_lens.data_ptr(), float(softmax_scale), float(q_scale), float(kv_scale), out.data_ptr(),
+                      lse.data_ptr() if lse is not None else None, workspace.data_ptr(), workspace.numel(), stream,
+                      ctypes.byref(self._opts))
+        self._fn = lib().mla_decode_ex
+        _check(self._fn(*self._args))
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != 0:
+            _check(rc)
 
 
 def kv_pack_quantize_fp8(latent, rope, kv_scale: float, *, slot_mapping=None, out=None, stream=None):

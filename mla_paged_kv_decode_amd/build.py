@@ -53,6 +53,33 @@ def parse_resources(text: str) -> dict:
     return kernels
 
 
+def lint_assembly() -> None:
+    """Compile the kernels to gfx950 assembly and check the inline-asm MFMA hazards (asm_lint)."""
+    import tempfile
+
+    sys.path.insert(0, HERE)
+    import asm_lint
+
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "mla_kernels.s")
+        cmd = [_hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "--cuda-device-only", "-S",
+               "-I", os.path.join(ROOT, "include"), "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-Wno-inline-asm", SOURCES[0], "-o", out]
+        proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if proc.returncode != 0:
+            sys.stderr.write(proc.stdout)
+            raise RuntimeError(f"hipcc -S failed ({proc.returncode})")
+        with open(out) as f:
+            report = asm_lint.lint(f.read())
+    bad = {k: v for k, v in report.items() if v}
+    if not report:
+        raise RuntimeError("asm lint found no split-KV kernel in the assembly")
+    if bad:
+        for k, v in bad.items():
+            sys.stderr.write(f"{k}:\n  " + "\n  ".join(v[:20]) + "\n")
+        raise RuntimeError("MFMA hazards in the generated assembly (see above)")
+
+
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), *FLAGS, *SOURCES, "-o", tmp]
@@ -60,6 +87,11 @@ def build(verbose: bool = False) -> str:
     if proc.returncode != 0:
         sys.stderr.write(proc.stdout)
         raise RuntimeError(f"hipcc failed ({proc.returncode})")
+    try:
+        lint_assembly()
+    except Exception:
+        os.remove(tmp)
+        raise
     os.replace(tmp, LIB)
     res = parse_resources(proc.stdout)
     lines = []

@@ -153,6 +153,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t* bt, const int32_t* seq_lens,
                 float softmax_scale, float q_scale, float kv_scale, void* out, float* lse, void* ws, size_t ws_bytes,
                 void* stream, const mla_options* opt) {
+  if (opt && (opt->stages < 0 || opt->stages > 2)) return fail(MLA_ERR_SHAPE, "options.stages must be 0, 1 or 2");
   if (!s) return fail(MLA_ERR_NULL, "shape is NULL");
   if (s->dtype == MLA_DTYPE_FP16) return fail(MLA_ERR_UNSUPPORTED, "fp16 inputs are not supported");
   if (s->dtype != MLA_DTYPE_BF16 && s->dtype != MLA_DTYPE_FP8_E4M3)
@@ -225,13 +226,17 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
   p.part_bf16 = pl.part_bf16;
   const int tile = dt == mla::kFp8 ? 64 : 32;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = mla::launch_partial(p, dt, s->page_size >= tile, st);
-  if (e != hipSuccess) return fail(MLA_ERR_HIP, "split-KV partial kernel launch failed: %s", hipGetErrorString(e));
+  const int stages = opt ? opt->stages : 0;
+  hipError_t e = hipSuccess;
+  if (stages != 2) {
+    e = mla::launch_partial(p, dt, s->page_size >= tile, st);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "split-KV partial kernel launch failed: %s", hipGetErrorString(e));
+  }
   if (opt && opt->split_event) {
     e = hipEventRecord((hipEvent_t)opt->split_event, st);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipEventRecord(split_event) failed: %s", hipGetErrorString(e));
   }
-  if (pl.G > 1) {
+  if (pl.G > 1 && stages != 1) {
     mla::CombineParams c{};
     c.part_o = p.part_o;
     c.part_lse = p.part_lse;

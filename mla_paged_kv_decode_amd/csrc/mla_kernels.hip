@@ -90,11 +90,13 @@ __device__ __forceinline__ uint32_t lds_addr(const lds_t* p) { return (uint32_t)
 // 1 KiB of LDS starting at m0.  Issued through inline asm so that the
 // compiler neither waits on it nor reorders LDS accesses around it (memory
 // clobber); completion is tracked by hand with vmcnt.
+// (an SALU write of M0 needs one wait state before a load that writes LDS)
 __device__ __forceinline__ void dma16_sbase(uint32_t voff, const void* sbase, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
 }
 __device__ __forceinline__ void dma16_vaddr(const void* vaddr, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(vaddr), "s"(m0) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(vaddr), "s"(m0) : "memory", "m0");
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight,
@@ -122,19 +124,21 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // kernel, and the 256 AGPRs are exactly the 32x512 fp32 output accumulator.
 // The compiler does not model hazards of asm MFMAs and takes their results as
 // written when the asm issues, while the hardware writes them some 64 cycles
-// later.  Each MFMA therefore starts with a short s_nop (VALU-written
-// operands), and the last MFMA of a chain carries the wait states that must
+// later.  The last MFMA of a chain therefore carries the wait states that must
 // pass before anything (a VALU use, or a copy the register allocator may
-// insert) reads the accumulator, inside the same asm statement.
+// insert) reads the accumulator, inside the same asm statement.  The fp8 score
+// MFMAs read only LDS-loaded, global-loaded and MFMA-written registers, so they
+// need no wait states before them; the bf16 ones take operands the compiler
+// may assemble with VALU moves, hence their leading s_nop.
 __device__ __forceinline__ void qk_mfma_f8(v16f& acc, const v8i& a, const v8i& b, bool last) {
   if (last) {
     asm volatile(
-        "s_nop 2\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]\n\t"
+        "v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]\n\t"
         "s_nop 7\n\ts_nop 7\n\ts_nop 7"
         : "+v"(acc)
         : "v"(a), "v"(b), "v"(127));
   } else {
-    asm volatile("s_nop 2\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
                  : "+v"(acc)
                  : "v"(a), "v"(b), "v"(127));
   }
@@ -142,7 +146,7 @@ __device__ __forceinline__ void qk_mfma_f8(v16f& acc, const v8i& a, const v8i& b
 // first MFMA of a chain: accumulator input is zero.  The output is early-clobber:
 // a multi-pass MFMA must not write registers that hold its own A or B operand.
 __device__ __forceinline__ void qk_mfma_f8_first(v16f& acc, const v8i& a, const v8i& b) {
-  asm volatile("s_nop 2\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0]"
+  asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0]"
                : "=&v"(acc)
                : "v"(a), "v"(b), "v"(127));
 }
@@ -822,7 +826,9 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   if constexpr (DT == kFp8) {
     // Wave w holds O^T for latent dims [128w, 128w+128) of all 128 rows; the
     // row owners publish 1/l, then the whole 128x512 tile is staged in LDS and
-    // written row-contiguous (whole 128-byte lines per store).
+    // written row-contiguous (whole 128-byte lines per store).  The stores are
+    // non-temporal: left dirty in L2 they would be written back at kernel end,
+    // delaying the merge kernel's start.
     asm volatile("" : "+v"(lane));
     const int ne = lane & 31, he = lane >> 5;
     const float l_tot = xor32_sum(l_acc);
@@ -864,7 +870,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         const int m_r = row0 + row;
         if (m_r < p.H_eff) {
           const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
-          *(v4i*)(dst + rowb * kDv + 8 * lane) = v;
+          __builtin_nontemporal_store(v, (v4i*)(dst + rowb * kDv + 8 * lane));
         }
       }
     } else {
@@ -895,7 +901,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           const int m_r = row0 + row;
           if (m_r < p.H_eff) {
             const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
-            *(v4f*)(dst + rowb * kDv + 256 * h + 4 * lane) = v;
+            __builtin_nontemporal_store(v, (v4f*)(dst + rowb * kDv + 256 * h + 4 * lane));
           }
         }
         lds_barrier();
@@ -949,7 +955,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         const int m_r = wrow0 + r;
         if (m_r < p.H_eff) {
           const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
-          *(v4i*)(dst + rowb * kDv + 256 * pass + 8 * ch) = v;
+          __builtin_nontemporal_store(v, (v4i*)(dst + rowb * kDv + 256 * pass + 8 * ch));
         }
       }
     }
@@ -973,7 +979,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         const int m_r = wrow0 + r;
         if (m_r < p.H_eff) {
           const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
-          *(v4f*)(dst + rowb * kDv + 256 * pass + 4 * lane) = v;
+          __builtin_nontemporal_store(v, (v4f*)(dst + rowb * kDv + 256 * pass + 4 * lane));
         }
       }
     }

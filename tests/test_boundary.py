@@ -117,6 +117,29 @@ def test_validation_errors_without_device():
     assert b"page_size" in mla.lib().mla_last_error()
 
 
+def test_options_layout_matches_header():
+    # mla_options: five int32 fields, four reserved int32, then a pointer at byte 32
+    o = mla.MlaOptions
+    assert [o.num_splits.offset, o.no_fold.offset, o.partial_fp32.offset, o.stages.offset, o.reserved.offset,
+            o.split_event.offset] == [0, 4, 8, 12, 16, 32]
+    assert ctypes.sizeof(o) == 40
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct mla_options"):text.index("} mla_options;")]
+    fields = re.findall(r"(int32_t|void\*)\s+(\w+)(\[\d+\])?;", body)
+    assert [f[1] for f in fields] == ["num_splits", "no_fold", "partial_fp32", "stages", "reserved", "split_event"]
+
+
+def test_stages_option_validated_before_any_device_work():
+    L = mla.lib()
+    shape = _shape()
+    for bad in (-1, 3):
+        opts = mla.options(stages=bad)
+        rc = L.mla_decode_ex(ctypes.byref(shape), 16, 16, 16, 16, 1.0, 1.0, 1.0, 16, 16, None, 0, None,
+                             ctypes.byref(opts))
+        assert rc == -3
+        assert b"stages" in L.mla_last_error()
+
+
 def test_pack_validation_without_device():
     L = mla.lib()
     assert L.mla_kv_pack_quantize_fp8(16, 512, 16, 64, None, -1, 1.0, 16, 10, None) == -3

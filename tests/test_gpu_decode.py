@@ -284,3 +284,24 @@ def test_empty_slices_ignore_stale_workspace(dtype):
                           workspace=wsb, opts=opts)
     torch.cuda.synchronize()
     assert_parity(x, out, lse, run_oracle(x))
+
+
+def test_stages_split_then_merge_equals_one_call():
+    """The split-KV kernel alone, then the merge alone on the same workspace, gives the one-call result bit-exactly."""
+    x = mi.make_inputs(3, 4, 32, mi.FP8_E4M3, ("list", [900, 2000, 64]), seed=57)
+    q, kv, bt, sl = to_dev(x)
+    ns, wsb = mla.plan(x.B, x.q_len, x.H, x.max_seq_len)
+    assert ns > 1
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
+    o1, l1 = mla.decode(q, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_seq_len=x.max_seq_len,
+                        workspace=ws)
+    ws2 = torch.full((wsb,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    o2 = torch.full_like(o1, float("nan"))
+    l2 = torch.full_like(l1, float("nan"))
+    mla.decode(q, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_seq_len=x.max_seq_len, out=o2, lse=l2,
+               workspace=ws2, opts=mla.options(stages=1))
+    mla.decode(q, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_seq_len=x.max_seq_len, out=o2, lse=l2,
+               workspace=ws2, opts=mla.options(stages=2))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
