@@ -492,8 +492,19 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           const float a4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
           return fmaxf(fmaxf(fmaxf(a0, a1), a2), fmaxf(fmaxf(a3, a4), x[15]));
         };
-        auto p_elem = [&](int idx) -> float {
-          return __builtin_amdgcn_exp2f(__builtin_fmaf(s0[idx], p.s_scale_log2, -pe_off));
+        // The exponentials run as a three-stage pipeline across MFMA slots
+        // (fma in one slot, exp2 in the next, sum and fp8 pack in the one after),
+        // so the VALU work inside a slot has no dependency chain to wait on.
+        float ya[2], yb[2], qa[2], qb[2];  // pair stages: fma results, exp2 results
+        auto pack_pair = [&](float p0, float p1, int pair, int* words) {
+          // pair j holds elements 2j, 2j+1: even pairs fill the low half of word j/2, odd pairs the high
+          if ((pair & 1) == 0) {
+            w_hold = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+            fence_v(w_hold);
+          } else {
+            words[pair >> 1] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, w_hold, true);
+            fence_v(words[pair >> 1]);
+          }
         };
         auto part_a = [&](int slot, int key0, bool need_mask) {
           if (slot == 0) {
@@ -536,58 +547,57 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             lsum = 0.f;
             fence_v(pe_off);
             fence_v(pe_e);
-          } else if (slot >= 4 && slot < 8) {
-            const int q = slot - 4;  // elements 2q, 2q+1 of s0
+          } else if (slot >= 4 && slot < 14) {
+            // P of keys 0..31 (elements of s0) in pairs: slot 4+t sums/packs pair t-2,
+            // exponentiates pair t-1 and scales pair t
+            const int t = slot - 4;
             fence_v(s0);
-            const float p0 = p_elem(2 * q), p1 = p_elem(2 * q + 1);
-            lsum += p0 + p1;
-            fence_v(lsum);
-            if ((q & 1) == 0) {
-              w_hold = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-              fence_v(w_hold);
-            } else {
-              pa[q >> 1] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, w_hold, true);
-              fence_v(pa[q >> 1]);
+            if (t >= 2) {
+              const int j = t - 2;
+              lsum += qa[j & 1] + qb[j & 1];
+              fence_v(lsum);
+              pack_pair(qa[j & 1], qb[j & 1], j, pa);
             }
-          } else if (slot >= 8) {
-            const int idx = slot;  // elements 8..15 of s0, one per slot
-            fence_v(s0);
-            const float pv = p_elem(idx);
-            lsum += pv;
-            fence_v(lsum);
-            const int j = idx & 3;
-            if (j == 0 || j == 2) {
-              p_hold = pv;
-              fence_v(p_hold);
-            } else if (j == 1) {
-              w_hold = __builtin_amdgcn_cvt_pk_fp8_f32(p_hold, pv, 0, false);
-              fence_v(w_hold);
-            } else {
-              pa[idx >> 2] = __builtin_amdgcn_cvt_pk_fp8_f32(p_hold, pv, w_hold, true);
-              fence_v(pa[idx >> 2]);
+            if (t >= 1 && t <= 8) {
+              const int j = t - 1;
+              qa[j & 1] = __builtin_amdgcn_exp2f(ya[j & 1]);
+              qb[j & 1] = __builtin_amdgcn_exp2f(yb[j & 1]);
+              fence_v(qa[j & 1]);
+              fence_v(qb[j & 1]);
+            }
+            if (t <= 7) {
+              ya[t & 1] = __builtin_fmaf(s0[2 * t], p.s_scale_log2, -pe_off);
+              yb[t & 1] = __builtin_fmaf(s0[2 * t + 1], p.s_scale_log2, -pe_off);
+              fence_v(ya[t & 1]);
+              fence_v(yb[t & 1]);
             }
           }
         };
-        // softmax, second half: P of keys 32..63 (from hb), then the row sum
+        // softmax, second half (score slots 0..17): P of keys 32..63 (from hb), one
+        // element per slot through the same three stages, then the row sum
         auto part_b = [&](int slot) {
-          if (slot < 16) {
-            fence_v(hb);  // (in place: no copy)
-            const float x = hb[slot];
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(x, p.s_scale_log2, -pe_off));
-            lsum += pv;
+          fence_v(hb);  // (in place: no copy)
+          if (slot >= 2) {
+            const int k = slot - 2;  // sum and pack element k
+            lsum += qa[k & 1];
             fence_v(lsum);
-            const int j = slot & 3;
-            if (j == 0 || j == 2) {
-              p_hold = pv;
+            if ((k & 1) == 0) {
+              p_hold = qa[k & 1];
               fence_v(p_hold);
-            } else if (j == 1) {
-              w_hold = __builtin_amdgcn_cvt_pk_fp8_f32(p_hold, pv, 0, false);
-              fence_v(w_hold);
             } else {
-              pb[slot >> 2] = __builtin_amdgcn_cvt_pk_fp8_f32(p_hold, pv, w_hold, true);
-              fence_v(pb[slot >> 2]);
+              pack_pair(p_hold, qa[k & 1], k >> 1, pb);
             }
-          } else if (slot == 16) {
+          }
+          if (slot >= 1 && slot <= 16) {
+            const int k = slot - 1;
+            qa[k & 1] = __builtin_amdgcn_exp2f(ya[k & 1]);
+            fence_v(qa[k & 1]);
+          }
+          if (slot <= 15) {
+            ya[slot & 1] = __builtin_fmaf(hb[slot], p.s_scale_log2, -pe_off);
+            fence_v(ya[slot & 1]);
+          }
+          if (slot == 17) {
             l_acc += __builtin_ldexpf(lsum, -pe_e);
             fence_v(l_acc);
           }
@@ -631,28 +641,36 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           *(__attribute__((address_space(3))) int*)(smem + kPScaleOffset + 16 * lane + 4 * wave) = 127 - pe_e;
         };
         // O^T += V^T P^T for this wave's 128 latent dims (4 blocks of 32) and all
-        // four row blocks: each transposed V read feeds four MFMAs
+        // four row blocks: each transposed V read feeds four MFMAs.  Accumulator
+        // o[4j + rr] holds latent block j of row block (wave + rr) & 3, so every
+        // block's MFMAs start with this wave's own rows, whose P is still in
+        // registers, and the other waves' P has a full MFMA to arrive.  The first
+        // V block is read before the P barrier (its stage landed long ago).
+        v8i vb[2];
+        auto pv_prefetch = [&](const lds_t* st) { vb[0] = vread(st, 4 * wave); };
         auto pv_chain = [&](const lds_t* st, bool with_a, int key0, bool need_mask) {
           v8i pt[4];
+          int psc[4];
+          pt[0] = v8i{pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+          psc[0] = 127 - pe_e;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
+          for (int rr = 1; rr < 4; ++rr) {
+            const int r = (wave + rr) & 3;
             const v4i x = *(const lds_v4i*)(smem + kPOffset + r * 2048 + 16 * lane);
             const v4i y = *(const lds_v4i*)(smem + kPOffset + r * 2048 + 1024 + 16 * lane);
-            pt[r] = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+            pt[rr] = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+            psc[rr] = *(const __attribute__((address_space(3))) int*)(smem + kPScaleOffset + 16 * lane + 4 * r);
           }
-          const v4i psc = *(const lds_v4i*)(smem + kPScaleOffset + 16 * lane);
-          v8i vb[2];
-          vb[0] = vread(st, 4 * wave);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (r == 0 && j + 1 < 4) vb[(j + 1) & 1] = vread(st, 4 * wave + j + 1);
+            for (int rr = 0; rr < 4; ++rr) {
+              if (rr == 0 && j + 1 < 4) vb[(j + 1) & 1] = vread(st, 4 * wave + j + 1);
               fence_v(vb[j & 1]);
-              o[4 * j + r] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb[j & 1], pt[r], o[4 * j + r], 0, 0, 0,
-                                                                             127, 0, psc[r]);
-              pin_agpr(o[4 * j + r]);
-              if (with_a) part_a(4 * j + r, key0, need_mask);
+              o[4 * j + rr] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb[j & 1], pt[rr], o[4 * j + rr], 0, 0,
+                                                                               0, 127, 0, psc[rr]);
+              pin_agpr(o[4 * j + rr]);
+              if (with_a) part_a(4 * j + rr, key0, need_mask);
               __builtin_amdgcn_sched_barrier(0);
             }
           }
@@ -691,14 +709,16 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           hb = s1;
           qk_chain(stage(t), true);  // also finishes the softmax of tile t-1
           p_publish();
+          pv_prefetch(stage(t - 1));
           lds_barrier();  // P of tile t-1 from all waves is visible
           const int key0 = k0 + t * TILE;
           pv_chain(stage(t - 1), true, key0, key0 + TILE > lim_min);
         }
         hb = s1;
 #pragma unroll
-        for (int slot = 0; slot < 17; ++slot) part_b(slot);
+        for (int slot = 0; slot < 18; ++slot) part_b(slot);
         p_publish();
+        pv_prefetch(stage(ntiles - 1));
         lds_barrier();
         pv_chain(stage(ntiles - 1), false, 0, false);
         // the dummy loads of the last two iterations must land before LDS is reused
@@ -840,9 +860,10 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
     lds_barrier();  // every wave is done with the KV ring and the P buffer
     if (he == 0) s_inv[32 * wave + ne] = inv;
     lds_barrier();
+    // accumulator rr of every latent block holds row block (wave + rr) & 3
     float invr[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) invr[r] = s_inv[32 * r + ne];
+    for (int rr = 0; rr < 4; ++rr) invr[rr] = s_inv[32 * ((wave + rr) & 3) + ne];
     const bool f32out = !sg.single && !p.part_bf16;
     const int row0 = mt * kTileM;
     if (!f32out) {
@@ -851,13 +872,13 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int rr = 0; rr < 4; ++rr) {
 #pragma unroll
           for (int gq = 0; gq < 4; ++gq) {
-            const int row = 32 * r + ne, col = 128 * wave + 32 * j + 8 * gq + 4 * he;
-            const v16f& acc = o[4 * j + r];
-            const v2i w = v2i{(int)pack_bf16x2(acc[4 * gq + 0] * invr[r], acc[4 * gq + 1] * invr[r]),
-                              (int)pack_bf16x2(acc[4 * gq + 2] * invr[r], acc[4 * gq + 3] * invr[r])};
+            const int row = 32 * ((wave + rr) & 3) + ne, col = 128 * wave + 32 * j + 8 * gq + 4 * he;
+            const v16f& acc = o[4 * j + rr];
+            const v2i w = v2i{(int)pack_bf16x2(acc[4 * gq + 0] * invr[rr], acc[4 * gq + 1] * invr[rr]),
+                              (int)pack_bf16x2(acc[4 * gq + 2] * invr[rr], acc[4 * gq + 3] * invr[rr])};
             *(lds_v2i*)(smem + row * kEpiPitch + 2 * col) = w;
           }
         }
@@ -881,14 +902,14 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
+            for (int rr = 0; rr < 4; ++rr) {
 #pragma unroll
               for (int gq = 0; gq < 4; ++gq) {
-                const int row = 32 * r + ne, col = 128 * (wave & 1) + 32 * j + 8 * gq + 4 * he;
-                const v16f& acc = o[4 * j + r];
+                const int row = 32 * ((wave + rr) & 3) + ne, col = 128 * (wave & 1) + 32 * j + 8 * gq + 4 * he;
+                const v16f& acc = o[4 * j + rr];
                 *(__attribute__((address_space(3))) v4f*)(smem + row * kEpiPitch + 4 * col) =
-                    v4f{acc[4 * gq + 0] * invr[r], acc[4 * gq + 1] * invr[r], acc[4 * gq + 2] * invr[r],
-                        acc[4 * gq + 3] * invr[r]};
+                    v4f{acc[4 * gq + 0] * invr[rr], acc[4 * gq + 1] * invr[rr], acc[4 * gq + 2] * invr[rr],
+                        acc[4 * gq + 3] * invr[rr]};
               }
             }
           }
