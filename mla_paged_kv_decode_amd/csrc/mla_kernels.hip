@@ -51,7 +51,11 @@ constexpr int kDummyOffset = kStages * kStageBytes;
 // per-row MFMA scales (4 per lane), shared by all waves
 constexpr int kPOffset = kDummyOffset + 1024;
 constexpr int kPScaleOffset = kPOffset + 4 * 2048;
-constexpr int kLdsBytes = kPScaleOffset + 1024;
+// block-table entries of the current segment, kBtEntries at a time
+constexpr int kBtOffset = kPScaleOffset + 1024;
+constexpr int kBtEntries = 256;
+constexpr int kLdsBytes = kBtOffset + 4 * kBtEntries;
+static_assert(kBtEntries == kThreads, "one block-table entry per thread per refill");
 // fp8 epilogue staging: 128 rows, pitch 1 KiB + 16 bytes
 constexpr int kEpiPitch = 1024 + 16;
 static_assert(kTileM * kEpiPitch <= kStages * kStageBytes, "epilogue staging must fit in the KV ring");
@@ -194,10 +198,29 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
-__device__ __forceinline__ long long wave_sum_ll(long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP moves (no LDS
+// traffic): shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then the
+// last lane of rows 0 and 2 is added into rows 1 and 3, and the last lane of
+// row 1 into rows 2 and 3.  64-bit values move as two 32-bit halves.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ long long dpp_move_ll(long long v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(v & 0xffffffffll), CTRL, ROWS, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(v >> 32), CTRL, ROWS, 0xf, true);
+  return (long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ long long wave_incl_scan_ll(long long v) {
+  v += dpp_move_ll<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_move_ll<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_move_ll<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_move_ll<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_move_ll<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_move_ll<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
   return v;
+}
+__device__ __forceinline__ long long readlane_ll(long long v, int l) {
+  const int lo = __builtin_amdgcn_readlane((int)(v & 0xffffffffll), l);
+  const int hi = __builtin_amdgcn_readlane((int)(v >> 32), l);
+  return (long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -268,28 +291,23 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
 
   // ---- Q rows into registers, laid out as the B operand of S^T = K Q^T ----
   // (invalid rows read row 0 of the group and are zeroed: no divergent branches)
+  // fp8 Q takes the direct-to-LDS path at the start of the tile pipeline below;
+  // bf16 Q (twice the bytes: the whole ring) is loaded here.
   constexpr int QSTEPS = (DT == kFp8) ? 9 : 36;
   v8i qreg[QSTEPS];
-  {
+  if constexpr (DT == kBf16) {
     const size_t qrow_idx = ((size_t)sg.b * p.q_len + gF) * p.H + (size_t)(row_valid ? m : 0);
     const uint8_t* qrow = p.q + qrow_idx * kDqk * ESZ;
     const int keep = row_valid ? -1 : 0;
 #pragma unroll
     for (int c = 0; c < QSTEPS; ++c) {
-      if constexpr (DT == kFp8) {
-        const v4i* src = (const v4i*)(qrow + 64 * c + 32 * hh);
-        const v4i x0 = src[0] & keep, x1 = src[1] & keep;
-        qreg[c] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-      } else {
-        const v4i x = *(const v4i*)(qrow + 2 * (16 * c + 8 * hh)) & keep;
-        qreg[c] = v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0};
-      }
+      const v4i x = *(const v4i*)(qrow + 2 * (16 * c + 8 * hh)) & keep;
+      qreg[c] = v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0};
     }
+    // Q must be in registers before the KV ring starts: the compiler cannot see the
+    // asynchronous LDS loads, so its own wait for Q would otherwise drain the ring.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0), expcnt/lgkmcnt unconstrained
   }
-
-  // Q must be in registers before the KV ring starts: the compiler cannot see the
-  // asynchronous LDS loads, so its own wait for Q would otherwise drain the ring.
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0), expcnt/lgkmcnt unconstrained
 
   v16f o[16];
   float m_ref = -INFINITY;  // reference the accumulators are relative to (log2 units)
@@ -320,8 +338,24 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
       dgeo[kk] = ((uint32_t)row << 16) | (uint32_t)(row * RB + col);
     }
 
-    auto page_raw = [&](int pidx) -> int { return bt[min(pidx, plast)]; };
-    auto clamp_page = [&](int pg) -> int { return min(max(pg, 0), p.num_pages - 1); };
+    // The segment's block-table entries are staged in LDS (kBtEntries at a
+    // time, refilled when the tiles run past them) and read from there one
+    // tile ahead.  A scalar load in the loop would make the next wait for LDS
+    // data wait for the scalar load as well (they share a counter and the
+    // scalar one completes out of order).
+    typedef __attribute__((address_space(3))) int lds_i32;
+    int bt_base = 0;
+    auto bt_fill = [&](int first) {
+      bt_base = first;
+      const int v = bt[min(first + 64 * wave + lane, plast)];
+      lds_barrier();  // every wave is done with the previous entries
+      *(lds_i32*)(smem + kBtOffset + 4 * (64 * wave + lane)) = v;
+      lds_barrier();
+    };
+    auto page_raw = [&](int pidx) -> int { return *(const lds_i32*)(smem + kBtOffset + 4 * (min(pidx, plast) - bt_base)); };
+    auto clamp_page = [&](int pg) -> int {
+      return min(max(__builtin_amdgcn_readfirstlane(pg), 0), p.num_pages - 1);
+    };
 
     // Scalar state of the tile whose loads are being issued.  Block-table
     // entries are read one tile ahead, so the scalar-load wait lands at the
@@ -336,6 +370,11 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
     int pf0 = 0, pf1 = 0, pf2 = 0, pf3 = 0;
     auto prefetch_pages = [&](int tt) {
       const int pidx0 = (k0 + tt * TILE) >> p.page_shift;
+      // refill at fixed tile counts (a test of bt_base here would make the DMA
+      // addresses look divergent to the compiler): a tile needs at most one
+      // entry when pages are at least a tile long, at most four otherwise
+      constexpr int kFillTiles = FAST ? kBtEntries : (kBtEntries - 3) / 4;
+      if (tt > 0 && tt % kFillTiles == 0) bt_fill(pidx0);
       pf0 = page_raw(pidx0);
       if constexpr (!FAST) {
         pf1 = page_raw(pidx0 + 1);
@@ -448,8 +487,8 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           pin_agpr(o[i]);
         }
       }
-      // all waves are done with the previous use of the LDS ring
-      lds_barrier();
+      // all waves are done with the previous use of the LDS ring (bt_fill starts with a barrier)
+      bt_fill(k0 >> p.page_shift);
       prefetch_pages(0);
 
       if constexpr (DT == kFp8) {
@@ -648,6 +687,19 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         // V block is read before the P barrier (its stage landed long ago).
         v8i vb[2];
         auto pv_prefetch = [&](const lds_t* st) { vb[0] = vread(st, 4 * wave); };
+        auto stage = [&](int t) -> const lds_t* { return smem + (t % kStages) * kStageBytes; };
+        // The segment's last tile was loaded whole: rows past its last key hold
+        // whatever follows in the page (possibly NaN).  Their scores are masked,
+        // but 0 * NaN would still reach O through the PV MFMA, so zero them.
+        auto zero_tail = [&](int t) {
+          const int nvalid = k1 - (k0 + t * TILE);
+          if (nvalid < TILE) {
+            lds_t* z = smem + (t % kStages) * kStageBytes + nvalid * RB;
+            const int nchunks = (TILE - nvalid) * (RB / 16);
+            for (int i = 64 * wave + lane; i < nchunks; i += kThreads) *(lds_v4i*)(z + 16 * i) = v4i{0, 0, 0, 0};
+            lds_barrier();
+          }
+        };
         auto pv_chain = [&](const lds_t* st, bool with_a, int key0, bool need_mask) {
           v8i pt[4];
           int psc[4];
@@ -675,25 +727,43 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             }
           }
         };
-        auto stage = [&](int t) -> const lds_t* { return smem + (t % kStages) * kStageBytes; };
-        // The segment's last tile was loaded whole: rows past its last key hold
-        // whatever follows in the page (possibly NaN).  Their scores are masked,
-        // but 0 * NaN would still reach O through the PV MFMA, so zero them.
-        auto zero_tail = [&](int t) {
-          const int nvalid = k1 - (k0 + t * TILE);
-          if (nvalid < TILE) {
-            lds_t* z = smem + (t % kStages) * kStageBytes + nvalid * RB;
-            const int nchunks = (TILE - nvalid) * (RB / 16);
-            for (int i = 64 * wave + lane; i < nchunks; i += kThreads) *(lds_v4i*)(z + 16 * i) = v4i{0, 0, 0, 0};
-            lds_barrier();
-          }
-        };
 
+        // Q: each wave's 32 rows (18 KiB, one contiguous block of the folded
+        // query) are copied straight into ring stages 2-3, which stay free
+        // until tile 2 is issued, so their latency overlaps that of tiles 0-1.
+        constexpr int kQDma = 32 * kDqk / 1024;  // 18 one-KiB loads per wave
+        {
+          const uint8_t* qblk = p.q + ((size_t)sg.b * p.q_len + gF) * p.H * kDqk;
+          const uint32_t qlds = smem_base + (uint32_t)(2 * kStageBytes + wave * 32 * kDqk);
+          int qlane = lane;
+          asm volatile("" : "+v"(qlane));  // addresses computed here, not kept live from the segment start
+#pragma unroll
+          for (int kk = 0; kk < kQDma; ++kk) {
+            const int o = 1024 * kk + 16 * qlane;
+            const int qn = o / kDqk;
+            const int mrow = mt * kTileM + 32 * wave + qn;
+            const int src_row = mrow < p.H_eff ? mrow : 0;
+            dma16_vaddr(qblk + (size_t)src_row * kDqk + (o - qn * kDqk),
+                        __builtin_amdgcn_readfirstlane(qlds + 1024u * (uint32_t)kk));
+          }
+        }
         // Every wave takes part in every tile: rows past H_eff score against
         // zero queries and are never stored.
         issue_tile(0);
         issue_tile(1);  // a dummy tile when the segment has one tile
-        wait_vm_barrier<kDmaPerWave>();  // tile 0 has landed
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kDmaPerWave) : "memory");  // this wave's Q has landed
+        {
+          const lds_t* qs = smem + 2 * kStageBytes + wave * 32 * kDqk + n * kDqk + 32 * hh;
+          const int keep = row_valid ? -1 : 0;
+#pragma unroll
+          for (int c = 0; c < QSTEPS; ++c) {
+            const v4i x0 = *(const lds_v4i*)(qs + 64 * c) & keep;
+            const v4i x1 = *(const lds_v4i*)(qs + 64 * c + 16) & keep;
+            qreg[c] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          }
+        }
+        // tile 0 has landed and every wave holds its Q: stages 2-3 may be refilled
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaPerWave) : "memory");
         if (ntiles == 1) zero_tail(0);
         dma_setup(2);
         qk_chain(stage(0), false);
@@ -1021,8 +1091,6 @@ template <int DT, bool FAST>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_split_kv_partial(PartialParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kLdsBytes];
-  __shared__ long long s_red[4];
-  __shared__ long long s_found[2];
   __shared__ int s_flag[4];
   lds_t* smem = (lds_t*)smem_raw;
 
@@ -1043,51 +1111,37 @@ mla_split_kv_partial(PartialParams p) {
   const int g = u % p.q_len_eff;
   const int mt = u / p.q_len_eff;
 
-  // ---- total work T (units) ----
-  long long local = 0;
-  for (int b = tid; b < p.B; b += kThreads) local += units_of(p.seq_lens[b]);
-  local = wave_sum_ll(local);
-  if (lane == 0) s_red[wave] = local;
-  __syncthreads();
-  const long long T = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+  // ---- total work T (units) and the slice's first sequence ----
+  // Every wave computes the same answer on its own (no LDS, no barrier): lane
+  // i sums the units of sequences [i*kper, (i+1)*kper), one wave-wide prefix
+  // sum gives T and each lane's first unit, and the lane whose range holds the
+  // slice's first unit is found by ballot.
+  cint_t* seq_lens = (cint_t*)p.seq_lens;
+  const int kper = (p.B + 63) >> 6;
+  const int bl0 = min(lane * kper, p.B), bl1 = min(bl0 + kper, p.B);
+  long long own = 0;
+  for (int bb = bl0; bb < bl1; ++bb) own += units_of(p.seq_lens[bb]);
+  const long long incl = wave_incl_scan_ll(own);
+  const long long T = readlane_ll(incl, 63);
   // the merge needs T to recognise empty slices (they write no partials)
   if (blockIdx.x == 0 && tid == 0 && p.meta != nullptr) *(long long*)(p.meta + 2 * p.B) = T;
   const long long t0 = slice_start(w, T, p.G), t1 = slice_start(w + 1, T, p.G);
   if (t0 >= t1) return;
-  __syncthreads();
-
-  // ---- first sequence of the slice: chunked block scan over sequences ----
-  long long base = 0;
-  if (tid == 0) s_found[0] = -1;
-  for (int start = 0; start < p.B; start += kThreads) {
-    const int b = start + tid;
-    const long long nb = b < p.B ? units_of(p.seq_lens[b]) : 0;
-    long long incl = nb;
-#pragma unroll
-    for (int o2 = 1; o2 < 64; o2 <<= 1) {
-      const long long y = __shfl_up(incl, o2, 64);
-      if (lane >= o2) incl += y;
-    }
-    __syncthreads();
-    if (lane == 63) s_red[wave] = incl;
-    __syncthreads();
-    long long woff = 0;
-    for (int k = 0; k < wave; ++k) woff += s_red[k];
-    const long long P = base + woff + incl - nb;
-    if (b < p.B && P <= t0 && t0 < P + nb) {
-      s_found[0] = b;
-      s_found[1] = P;
-    }
-    base += s_red[0] + s_red[1] + s_red[2] + s_red[3];
-    __syncthreads();
-    if (s_found[0] >= 0) break;
+  const long long excl = incl - own;
+  // every sequence has at least one unit, so t0 < T lies in exactly one non-empty lane range
+  const unsigned long long hit = __builtin_amdgcn_ballot_w64(own > 0 && excl <= t0 && t0 < incl);
+  const int hl = hit != 0 ? (int)__builtin_ctzll(hit) : 0;
+  long long P = readlane_ll(excl, hl);
+  int b = hl * kper;
+  while (b + 1 < p.B) {
+    const int nb = units_of(seq_lens[b]);
+    if (t0 < P + nb) break;
+    P += nb;
+    ++b;
   }
-  int b = (int)s_found[0];
-  long long P = s_found[1];
 
   // ---- segments of this slice ----
   long long cur = t0;
-  cint_t* seq_lens = (cint_t*)p.seq_lens;
   while (cur < t1 && b < p.B) {
     const int nb = units_of(seq_lens[b]);
     const long long seg_end = min(t1, P + nb);
