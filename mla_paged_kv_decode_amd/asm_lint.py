@@ -10,7 +10,10 @@ instantiation and reports:
     MFMA_RESULT_WAITS wait states have passed (a VALU use, a store, or a copy
     the register allocator inserted);
   * an MFMA that reads a VGPR written by a VALU instruction fewer than
-    VALU_TO_MFMA_WAITS wait states earlier.
+    VALU_TO_MFMA_WAITS wait states earlier;
+  * a scratch (spill) access inside the function's innermost loop: a spill
+    reload there is a vector-memory load, and waiting for it waits for every
+    KV tile load in flight, once per tile.
 
 Wait states are counted conservatively: one per instruction, N+1 per `s_nop N`;
 stalls are not credited.  A label resets the tracking (control flow merges).
@@ -83,11 +86,28 @@ def lint_function(lines: list[str]) -> list[str]:
     return problems
 
 
+def loop_spills(lines: list[str]) -> list[str]:
+    """Scratch accesses in blocks at the deepest loop level the compiler annotated."""
+    depth, deepest, found = 0, 0, []
+    for i, ln in enumerate(lines):
+        s = ln.strip()
+        m = re.match(r"^\.LBB\d+_\d+:.*Depth=(\d+)", s)
+        if m:
+            depth = int(m.group(1))
+            deepest = max(deepest, depth)
+        elif re.match(r"^\.LBB\d+_\d+:", s):
+            depth = 0
+        elif s.startswith("scratch_"):
+            found.append((depth, i, s))
+    return [f"line {i}: '{s[:60]}' inside the innermost loop" for d, i, s in found if deepest and d == deepest]
+
+
 def lint(asm_text: str, name_part: str = "mla_split_kv_partial") -> dict:
     """{function name: [problems]} for every function whose name contains name_part."""
     out = {}
     for chunk in re.split(r"\n(?=_Z\w+:)", asm_text):
         name = chunk.split(":", 1)[0]
         if name_part in name:
-            out[name] = lint_function(chunk.split("\n"))
+            lines = chunk.split("\n")
+            out[name] = lint_function(lines) + loop_spills(lines)
     return out

@@ -77,7 +77,7 @@ def lint_assembly() -> None:
     if bad:
         for k, v in bad.items():
             sys.stderr.write(f"{k}:\n  " + "\n  ".join(v[:20]) + "\n")
-        raise RuntimeError("MFMA hazards in the generated assembly (see above)")
+        raise RuntimeError("MFMA hazards or loop spills in the generated assembly (see above)")
 
 
 def build(verbose: bool = False) -> str:

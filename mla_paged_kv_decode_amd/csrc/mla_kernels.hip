@@ -338,11 +338,13 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
       dgeo[kk] = ((uint32_t)row << 16) | (uint32_t)(row * RB + col);
     }
 
-    // The segment's block-table entries are staged in LDS (kBtEntries at a
-    // time, refilled when the tiles run past them) and read from there one
+    // fp8: the segment's block-table entries are staged in LDS (kBtEntries at
+    // a time, refilled when the tiles run past them) and read from there one
     // tile ahead.  A scalar load in the loop would make the next wait for LDS
     // data wait for the scalar load as well (they share a counter and the
-    // scalar one completes out of order).
+    // scalar one completes out of order).  The bf16 path keeps scalar loads:
+    // its 144 Q registers leave no VGPR for the staged entry, and a spill
+    // reload in the loop would wait for every load in flight.
     typedef __attribute__((address_space(3))) int lds_i32;
     int bt_base = 0;
     auto bt_fill = [&](int first) {
@@ -352,7 +354,13 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
       *(lds_i32*)(smem + kBtOffset + 4 * (64 * wave + lane)) = v;
       lds_barrier();
     };
-    auto page_raw = [&](int pidx) -> int { return *(const lds_i32*)(smem + kBtOffset + 4 * (min(pidx, plast) - bt_base)); };
+    auto page_raw = [&](int pidx) -> int {
+      if constexpr (DT == kFp8) {
+        return *(const lds_i32*)(smem + kBtOffset + 4 * (min(pidx, plast) - bt_base));
+      } else {
+        return bt[min(pidx, plast)];
+      }
+    };
     auto clamp_page = [&](int pg) -> int {
       return min(max(__builtin_amdgcn_readfirstlane(pg), 0), p.num_pages - 1);
     };
@@ -374,7 +382,9 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
       // addresses look divergent to the compiler): a tile needs at most one
       // entry when pages are at least a tile long, at most four otherwise
       constexpr int kFillTiles = FAST ? kBtEntries : (kBtEntries - 3) / 4;
-      if (tt > 0 && tt % kFillTiles == 0) bt_fill(pidx0);
+      if constexpr (DT == kFp8) {
+        if (tt > 0 && tt % kFillTiles == 0) bt_fill(pidx0);
+      }
       pf0 = page_raw(pidx0);
       if constexpr (!FAST) {
         pf1 = page_raw(pidx0 + 1);
@@ -488,7 +498,11 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         }
       }
       // all waves are done with the previous use of the LDS ring (bt_fill starts with a barrier)
-      bt_fill(k0 >> p.page_shift);
+      if constexpr (DT == kFp8) {
+        bt_fill(k0 >> p.page_shift);
+      } else {
+        lds_barrier();
+      }
       prefetch_pages(0);
 
       if constexpr (DT == kFp8) {
