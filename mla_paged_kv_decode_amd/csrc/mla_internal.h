@@ -59,6 +59,9 @@ struct PackParams {
 
 // Launchers (defined in mla_kernels.hip).  Return the launch's hipError_t.
 hipError_t launch_partial(const PartialParams& p, int dtype, bool fast_pages, hipStream_t stream);
+// The merge runs one wave per output row when sequences span few slices on
+// average (G < 16 B), and one workgroup per row otherwise.
+inline bool combine_per_wave(int B, int G) { return (long long)G < 16LL * B; }
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_pack_fp8(const PackParams& p, hipStream_t stream);
 

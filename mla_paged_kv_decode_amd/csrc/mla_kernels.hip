@@ -48,7 +48,8 @@ static_assert(4 * kEpiWaveBytes <= kStages * kStageBytes, "epilogue staging must
 // 1 KiB LDS scratch after the ring: destination of the loads of dummy tiles
 constexpr int kDummyOffset = kStages * kStageBytes;
 // fp8 path: P of the four row blocks (B-operand layout, 2 KiB each) and their
-// per-row MFMA scales (4 per lane), shared by all waves
+// per-row MFMA scales (one dword per lane, wave-major so that every access is
+// conflict-free), shared by all waves
 constexpr int kPOffset = kDummyOffset + 1024;
 constexpr int kPScaleOffset = kPOffset + 4 * 2048;
 // block-table entries of the current segment, kBtEntries at a time
@@ -691,7 +692,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           lds_t* pw = smem + kPOffset + wave * 2048;
           *(lds_v4i*)(pw + 16 * lane) = v4i{pa[0], pa[1], pa[2], pa[3]};
           *(lds_v4i*)(pw + 1024 + 16 * lane) = v4i{pb[0], pb[1], pb[2], pb[3]};
-          *(__attribute__((address_space(3))) int*)(smem + kPScaleOffset + 16 * lane + 4 * wave) = 127 - pe_e;
+          *(__attribute__((address_space(3))) int*)(smem + kPScaleOffset + 256 * wave + 4 * lane) = 127 - pe_e;
         };
         // O^T += V^T P^T for this wave's 128 latent dims (4 blocks of 32) and all
         // four row blocks: each transposed V read feeds four MFMAs.  Accumulator
@@ -725,7 +726,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             const v4i x = *(const lds_v4i*)(smem + kPOffset + r * 2048 + 16 * lane);
             const v4i y = *(const lds_v4i*)(smem + kPOffset + r * 2048 + 1024 + 16 * lane);
             pt[rr] = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-            psc[rr] = *(const __attribute__((address_space(3))) int*)(smem + kPScaleOffset + 16 * lane + 4 * r);
+            psc[rr] = *(const __attribute__((address_space(3))) int*)(smem + kPScaleOffset + 256 * r + 4 * lane);
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -1261,6 +1262,98 @@ __global__ void __launch_bounds__(256) mla_combine(CombineParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Merge, one wave per output row (four rows per workgroup, no barriers): for
+// batches whose sequences span few slices, where a whole workgroup per row
+// would mostly wait.  Lane l owns latent dims [8l, 8l+8); slice weights are
+// computed by the lane of the slice and broadcast with readlane; four slices'
+// partial rows are in flight at a time.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) mla_combine_rows(CombineParams p) {
+  const int lane = threadIdx.x & 63;
+  const long long grow = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (grow >= (long long)p.B * p.rows_per_b) return;
+  const int b = (int)(grow / p.rows_per_b);
+  const int row = (int)(grow - (long long)b * p.rows_per_b);
+  const int w0 = max(p.meta[2 * b], 0), w1 = min(p.meta[2 * b + 1], p.G - 1);
+  if (w0 >= w1) return;  // single slice: written by the partial kernel
+  const int n = w1 - w0 + 1;
+  const long long T = *(const long long*)(p.meta + 2 * p.B);
+  auto lse_of = [&](int s) -> float {
+    if (slice_start(s, T, p.G) == slice_start(s + 1, T, p.G)) return -INFINITY;
+    return p.part_lse[(size_t)(s + b) * p.rows_per_b + row];
+  };
+  float mx = -INFINITY;
+  for (int i = lane; i < n; i += 64) mx = fmaxf(mx, lse_of(w0 + i));
+  mx = wave_max(mx);
+  float sum = 0.f;
+  if (mx > -INFINITY)
+    for (int i = lane; i < n; i += 64) sum += expf(lse_of(w0 + i) - mx);
+  sum = wave_sum(sum);
+  const float lse_out = mx > -INFINITY ? mx + logf(sum) : -INFINITY;
+
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  const size_t st_rows = (size_t)p.rows_per_b * kDv;  // elements between consecutive slots
+  const size_t base = ((size_t)(w0 + b) * p.rows_per_b + row) * kDv + 8 * lane;
+  // slots of empty slices hold stale bytes: select, never multiply them by 0
+  auto add_bf16 = [&](const v4i& x, float wgt) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t u = (uint32_t)x[e];
+      acc[2 * e] += wgt > 0.f ? wgt * __builtin_bit_cast(float, u << 16) : 0.f;
+      acc[2 * e + 1] += wgt > 0.f ? wgt * __builtin_bit_cast(float, u & 0xffff0000u) : 0.f;
+    }
+  };
+  auto add_f32 = [&](const v4f& x0, const v4f& x1, float wgt) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += wgt > 0.f ? wgt * x0[e] : 0.f;
+      acc[4 + e] += wgt > 0.f ? wgt * x1[e] : 0.f;
+    }
+  };
+  if (mx > -INFINITY) {
+    for (int c0 = 0; c0 < n; c0 += 64) {
+      const int cn = min(64, n - c0);
+      const float wl = lane < cn ? expf(lse_of(w0 + c0 + lane) - lse_out) : 0.f;
+      auto wgt_of = [&](int i) -> float {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), i));
+      };
+      int i = 0;
+      if (p.part_bf16) {
+        const uint16_t* src = (const uint16_t*)p.part_o + base + (size_t)c0 * st_rows;
+        for (; i + 4 <= cn; i += 4) {
+          v4i x[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) x[j] = *(const v4i*)(src + (size_t)(i + j) * st_rows);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) add_bf16(x[j], wgt_of(i + j));
+        }
+        for (; i < cn; ++i) add_bf16(*(const v4i*)(src + (size_t)i * st_rows), wgt_of(i));
+      } else {
+        const float* src = (const float*)p.part_o + base + (size_t)c0 * st_rows;
+        for (; i + 4 <= cn; i += 4) {
+          v4f x0[4], x1[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x0[j] = *(const v4f*)(src + (size_t)(i + j) * st_rows);
+            x1[j] = *(const v4f*)(src + (size_t)(i + j) * st_rows + 4);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) add_f32(x0[j], x1[j], wgt_of(i + j));
+        }
+        for (; i < cn; ++i)
+          add_f32(*(const v4f*)(src + (size_t)i * st_rows), *(const v4f*)(src + (size_t)i * st_rows + 4), wgt_of(i));
+      }
+    }
+  }
+  const v4i packed = v4i{(int)pack_bf16x2(acc[0], acc[1]), (int)pack_bf16x2(acc[2], acc[3]),
+                         (int)pack_bf16x2(acc[4], acc[5]), (int)pack_bf16x2(acc[6], acc[7])};
+  *(v4i*)(p.out + ((size_t)b * p.rows_per_b + row) * kDv + 8 * lane) = packed;
+  if (p.lse != nullptr && lane == 0) p.lse[(size_t)b * p.rows_per_b + row] = lse_out;
+}
+
+// ---------------------------------------------------------------------------
 // Pack + quantise: one thread per 8 elements of a 576-wide output row.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float quant_in(uint32_t bits16, float scale) {
@@ -1326,8 +1419,13 @@ hipError_t launch_partial(const PartialParams& p, int dtype, bool fast_pages, hi
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   const long long rows = (long long)p.B * p.rows_per_b;
-  const dim3 grid((unsigned)rows), block(256);
-  hipLaunchKernelGGL(mla_combine, grid, block, 0, stream, p);
+  if (combine_per_wave(p.B, p.G)) {
+    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    hipLaunchKernelGGL(mla_combine_rows, grid, block, 0, stream, p);
+  } else {
+    const dim3 grid((unsigned)rows), block(256);
+    hipLaunchKernelGGL(mla_combine, grid, block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -272,13 +272,20 @@ def test_packed_cache_feeds_decode():
     assert_parity(x, out, lse, run_oracle(x))
 
 
+# (B, lens, slices): 96 slices for 3 sequences merge with a workgroup per row, 64 for 8 sequences
+# with a wave per row (fewer than 16 slices per sequence)
+EMPTY_SLICE_CASES = [(3, [700, 5, 130], 96), (8, [700, 5, 130, 64, 1, 250, 0, 90], 64)]
+
+
 @pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
-def test_empty_slices_ignore_stale_workspace(dtype):
+@pytest.mark.parametrize("B,lens,splits", EMPTY_SLICE_CASES)
+def test_empty_slices_ignore_stale_workspace(dtype, B, lens, splits):
     """More KV slices than 64-key units: empty slices write nothing and the merge must skip them."""
-    x = mi.make_inputs(3, 4, 32, dtype, ("list", [700, 5, 130]), seed=121)
+    x = mi.make_inputs(B, 4, 32, dtype, ("list", lens), seed=121 + B)
+    print(f"B={B} lens={lens} splits={splits} dtype={dtype}", flush=True)
     q, kv, bt, sl = to_dev(x)
-    opts = mla.options(num_splits=96)
-    _, ws = mla.plan(3, 4, 32, x.max_seq_len, opts)
+    opts = mla.options(num_splits=splits)
+    _, ws = mla.plan(B, 4, 32, x.max_seq_len, opts)
     wsb = torch.full((ws,), 0xFF, dtype=torch.uint8, device="cuda:0")  # NaN everywhere
     out, lse = mla.decode(q, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_seq_len=x.max_seq_len,
                           workspace=wsb, opts=opts)
