@@ -55,7 +55,7 @@ def _load():
     p = ctypes.c_void_p
     i = ctypes.c_int
     d = ctypes.c_double
-    lib.oracle_mla_decode.argtypes = [p, p, i, p, i, p, i, i, i, i, i, d, d, d, i, p, p, p, i]
+    lib.oracle_mla_decode.argtypes = [p, p, i, p, i, p, i, i, i, i, i, d, d, d, i, i, p, p, p, i]
     lib.oracle_mla_decode.restype = i
     lib.oracle_dec_bf16.argtypes = [ctypes.c_uint16]
     lib.oracle_dec_bf16.restype = d
@@ -106,8 +106,8 @@ def fold_factor(q_len: int, H: int, tile_m: int = 128) -> int:
 
 
 def mla_decode(q, kv_cache, block_table, seq_lens, *, dtype: int, softmax_scale: float,
-               q_scale: float = 1.0, kv_scale: float = 1.0, split_len: int = 0, num_threads: int = 0,
-               want_absv: bool = False):
+               q_scale: float = 1.0, kv_scale: float = 1.0, split_len: int = 0, window: int = 0,
+               num_threads: int = 0, want_absv: bool = False):
     """fp64 MLA decode.
 
     q: uint16 (bf16 bits) or uint8 (e4m3 codes) array [B, q_len, H, 576].
@@ -115,6 +115,7 @@ def mla_decode(q, kv_cache, block_table, seq_lens, *, dtype: int, softmax_scale:
     block_table: int32 [B, max_pages]; seq_lens: int32 [B].
     Returns (O float64 [B, q_len, H, 512], LSE float64 [B, q_len, H]).
     split_len > 0 computes per-chunk partials and merges them by LSE.
+    window > 0 is the sliding-window mask: token t sees keys [max(0, n_t - window), n_t).
     want_absv=True also returns sum_j softmax_j * |V_j| (same shape as O): the
     scale of the output's sensitivity to rounding the softmax weights.
     """
@@ -137,7 +138,7 @@ def mla_decode(q, kv_cache, block_table, seq_lens, *, dtype: int, softmax_scale:
     absv = np.zeros((B, q_len, H, D_V), dtype=np.float64) if want_absv else None
     rc = lib.oracle_mla_decode(_ptr(q), _ptr(kv_cache), int(dtype), _ptr(block_table), int(block_table.shape[1]),
                                _ptr(seq_lens), B, q_len, H, num_pages, page_size, float(softmax_scale),
-                               float(q_scale), float(kv_scale), int(split_len), _ptr(out), _ptr(lse),
+                               float(q_scale), float(kv_scale), int(split_len), int(window), _ptr(out), _ptr(lse),
                                None if absv is None else _ptr(absv), int(num_threads))
     if rc == -1:
         raise IndexError("block_table entry out of range for a visible key")

@@ -17,6 +17,10 @@
  *     where L = seq_lens[b] (causal across the q_len new tokens; bottom-right
  *     alignment is the reading taken where the pages only say "causal",
  *     article section 4, static key list).
+ *   - Sliding window (TokenSpeed MLA article, section 6: the decode tests
+ *     include a sliding-window mask; the pages do not spell out its
+ *     convention): with window W > 0, token t sees only its last W visible
+ *     keys, j in [max(0, n_t - W), n_t).  W = 0 is the plain causal mask.
  *   - s_j = softmax_scale * sum_d qv[d] * kv[d], qv = q_scale * dec(q),
  *     kv = kv_scale * dec(row).  O = sum_j softmax(s)_j * V_j (first 512),
  *     LSE = ln sum_j exp(s_j) (natural log).  A row with no visible key gets
@@ -139,17 +143,18 @@ static int attend_range(const void* kv, int dtype, const int32_t* bt_row, int nu
  * seq_lens:   [B] int32
  * out:        [B, q_len, H, 512] fp64;  lse: [B, q_len, H] fp64
  * split_len:  0 = plain definition; > 0 = split/merge with chunks of that many keys
+ * window:     0 = causal; > 0 = token t sees keys [max(0, n_t - window), n_t)
  * absv:       optional [B, q_len, H, 512] fp64: sum_j softmax_j * |V_j[d]|, the scale of
  *             the output's sensitivity to per-weight rounding (unsplit mode only)
  * Returns 0 on success, -1 on a block_table entry out of range, -2 on bad arguments.
  */
 int oracle_mla_decode(const void* q, const void* kv, int dtype, const int32_t* block_table, int max_pages,
                       const int32_t* seq_lens, int B, int q_len, int H, int num_pages, int page_size,
-                      double softmax_scale, double q_scale, double kv_scale, int split_len,
+                      double softmax_scale, double q_scale, double kv_scale, int split_len, int window,
                       double* out, double* lse, double* absv, int num_threads) {
   if (!q || !kv || !block_table || !seq_lens || !out || !lse) return -2;
   if (dtype != ORC_BF16 && dtype != ORC_FP8_E4M3) return -2;
-  if (B < 0 || q_len <= 0 || H <= 0 || page_size <= 0 || max_pages < 0 || split_len < 0) return -2;
+  if (B < 0 || q_len <= 0 || H <= 0 || page_size <= 0 || max_pages < 0 || split_len < 0 || window < 0) return -2;
   if (absv && split_len > 0) return -2;
   for (int b = 0; b < B; ++b) {
     if (seq_lens[b] < 0 || (seq_lens[b] + page_size - 1) / page_size > max_pages) return -2;
@@ -167,7 +172,8 @@ int oracle_mla_decode(const void* q, const void* kv, int dtype, const int32_t* b
     int n = L - q_len + t + 1;
     if (n < 0) n = 0;
     if (n > L) n = L;
-    int chunk = split_len > 0 ? split_len : (n > 0 ? n : 1);
+    int lo = (window > 0 && n > window) ? n - window : 0; /* first visible key */
+    int chunk = split_len > 0 ? split_len : (n - lo > 0 ? n - lo : 1);
     size_t row0 = ((size_t)b * q_len + t) * H;
     double* qv = (double*)malloc(sizeof(double) * (size_t)H * ORC_D_QK);
     double* row = (double*)malloc(sizeof(double) * ORC_D_QK);
@@ -179,17 +185,17 @@ int oracle_mla_decode(const void* q, const void* kv, int dtype, const int32_t* b
     for (int h = 0; h < H; ++h) decode_row(q, dtype, (row0 + h) * ORC_D_QK, ORC_D_QK, q_scale, qv + (size_t)h * ORC_D_QK);
     const int32_t* bt_row = block_table + (size_t)b * max_pages;
     if (split_len == 0) {
-      if (attend_range(kv, dtype, bt_row, num_pages, page_size, 0, n, H, qv, softmax_scale, kv_scale, scores, row,
+      if (attend_range(kv, dtype, bt_row, num_pages, page_size, lo, n, H, qv, softmax_scale, kv_scale, scores, row,
                        o_acc, lse_acc, absv ? absv + row0 * ORC_D_V : NULL) != 0)
         st = -1;
     } else {
       /* chunk partials, then the LSE-weighted merge */
-      int nsplit = (n + chunk - 1) / chunk;
+      int nsplit = (n - lo + chunk - 1) / chunk;
       if (nsplit == 0) nsplit = 1;
       double* all_o = (double*)malloc(sizeof(double) * (size_t)nsplit * H * ORC_D_V);
       double* all_l = (double*)malloc(sizeof(double) * (size_t)nsplit * H);
       for (int s = 0; s < nsplit && st == 0; ++s) {
-        int j0 = s * chunk, j1 = j0 + chunk < n ? j0 + chunk : n;
+        int j0 = lo + s * chunk, j1 = j0 + chunk < n ? j0 + chunk : n;
         if (attend_range(kv, dtype, bt_row, num_pages, page_size, j0, j1, H, qv, softmax_scale, kv_scale, scores, row,
                          all_o + (size_t)s * H * ORC_D_V, all_l + (size_t)s * H, NULL) != 0)
           st = -1;

@@ -2,8 +2,8 @@
 
 It shares nothing with ``oracle/``: stored values are decoded with torch's
 own bf16 / float8_e4m3fn conversions, the paged cache is first gathered into
-a dense [L, 576] key matrix in logical order, the causal mask is an explicit
-boolean matrix, and the softmax / log-sum-exp come from scipy.
+a dense [L, 576] key matrix in logical order, the causal (and sliding-window)
+mask is an explicit boolean matrix, and the softmax / log-sum-exp come from scipy.
 """
 import numpy as np
 import scipy.special
@@ -25,7 +25,7 @@ def dense_keys(kv: np.ndarray, block_table: np.ndarray, b: int, L: int) -> np.nd
     return np.stack(rows) if rows else np.zeros((0, kv.shape[2]))
 
 
-def brute_decode(x: "mi.DecodeInputs", *, alignment: str = "bottom_right"):
+def brute_decode(x: "mi.DecodeInputs", *, alignment: str = "bottom_right", window: int = 0):
     q = decode_values(x.q, x.dtype) * x.q_scale
     kv = decode_values(x.kv_cache, x.dtype) * x.kv_scale
     B, q_len, H, _ = q.shape
@@ -43,6 +43,8 @@ def brute_decode(x: "mi.DecodeInputs", *, alignment: str = "bottom_right"):
             mask = j <= (L - q_len + t)
         else:  # the other reading of "causal": token t sees keys 0..t
             mask = j <= t
+        if window > 0:  # sliding window: only the last `window` keys a token can see
+            mask = mask & (j > (L - q_len + t) - window)
         scores = np.where(mask[:, None, :], scores, -np.inf)
         for tt in range(q_len):
             if not mask[tt].any():

@@ -6,7 +6,8 @@
   (tests/golden/fold_examples.txt);
 * the attention result against a dense scipy brute force on tiny shapes;
 * closed forms: zero query => LSE = ln(n_t) and O = mean of the visible V rows
-  (pins the causal alignment and the length handling per token);
+  (pins the causal alignment and the length handling per token), and the same
+  with a sliding window (pins both ends of each token's window);
 * invariants: split/merge at several chunk sizes, page relabelling, needles.
 """
 import math
@@ -159,6 +160,87 @@ def test_single_visible_key_is_exact():
     k = decode_values(x.kv_cache, x.dtype)[x.block_table[0, 0], 0] * x.kv_scale
     assert np.array_equal(O[0, 0], np.broadcast_to(k[:512], (4, 512)))
     assert np.allclose(lse[0, 0], x.softmax_scale * q[0, 0] @ k, rtol=1e-14)
+
+
+# ---------------------------------------------------------------- sliding window
+WINDOW_SHAPES = [
+    # B, q_len, H, dtype, lens, page_size, window
+    (2, 4, 4, mi.FP8_E4M3, [3, 200], 16, 1),
+    (3, 4, 2, mi.BF16, [0, 4, 300], 64, 5),
+    (2, 3, 5, mi.FP8_E4M3, [1, 130], 64, 64),
+    (1, 2, 8, mi.BF16, [257], 16, 100),
+    (2, 1, 3, mi.FP8_E4M3, [40, 77], 16, 1000),
+]
+
+
+@pytest.mark.parametrize("B,q_len,H,dtype,lens,ps,window", WINDOW_SHAPES)
+def test_window_matches_dense_brute_force(B, q_len, H, dtype, lens, ps, window):
+    x = mi.make_inputs(B, q_len, H, dtype, ("list", lens), page_size=ps, seed=61 + B + H)
+    O, lse = _run(x, window=window)
+    Ob, lseb = brute_decode(x, window=window)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lseb))
+    fin = np.isfinite(lseb)
+    assert np.allclose(lse[fin], lseb[fin], rtol=1e-12, atol=1e-12)
+    assert np.allclose(O, Ob, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("window", [1, 3, 20, 64])
+def test_window_zero_query_gives_log_count_and_mean(window):
+    # constant scores: LSE = ln(#keys in the window), O = mean of exactly those V rows,
+    # which pins both ends of every token's window
+    lens, q_len = [70, 2, 0, 129], 4
+    x = mi.make_inputs(len(lens), q_len, 3, mi.BF16, ("list", lens), page_size=16, seed=19)
+    x.q[:] = 0
+    O, lse = _run(x, window=window)
+    kv = decode_values(x.kv_cache, x.dtype)
+    for b, L in enumerate(lens):
+        K = dense_keys(kv, x.block_table, b, L)
+        for t in range(q_len):
+            n_t = min(max(L - q_len + t + 1, 0), L)
+            lo = max(0, n_t - window)
+            if n_t == 0:
+                assert np.all(np.isneginf(lse[b, t])) and np.all(O[b, t] == 0)
+                continue
+            assert np.allclose(lse[b, t], math.log(n_t - lo), rtol=0, atol=1e-14)
+            assert np.allclose(O[b, t], K[lo:n_t, :512].mean(axis=0)[None, :], rtol=1e-13, atol=1e-14)
+
+
+def test_window_of_one_is_the_diagonal_key():
+    x = mi.make_inputs(2, 4, 3, mi.FP8_E4M3, ("list", [9, 300]), page_size=16, seed=23)
+    O, lse = _run(x, window=1)
+    q = decode_values(x.q, x.dtype) * x.q_scale
+    kv = decode_values(x.kv_cache, x.dtype) * x.kv_scale
+    for b, L in enumerate([9, 300]):
+        K = dense_keys(kv, x.block_table, b, L)
+        for t in range(4):
+            j = L - 4 + t  # the only visible key
+            assert np.array_equal(O[b, t], np.broadcast_to(K[j, :512], (3, 512)))
+            assert np.allclose(lse[b, t], x.softmax_scale * q[b, t] @ K[j], rtol=1e-13)
+
+
+def test_window_covering_every_key_changes_nothing():
+    x = mi.make_inputs(3, 4, 4, mi.FP8_E4M3, ("list", [0, 90, 333]), page_size=16, seed=25)
+    O, lse = _run(x)
+    for window in (333, 334, 10 ** 6):
+        Ow, lsew = _run(x, window=window)
+        assert np.array_equal(O, Ow) and np.array_equal(lse, lsew)
+
+
+@pytest.mark.parametrize("split_len", [1, 7, 64])
+def test_window_split_merge_equals_unsplit(split_len):
+    x = mi.make_inputs(3, 4, 4, mi.BF16, ("list", [0, 90, 333]), page_size=16, seed=27)
+    O, lse = _run(x, window=50)
+    Os, lses = _run(x, split_len=split_len, window=50)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lses))
+    fin = np.isfinite(lse)
+    assert np.allclose(lse[fin], lses[fin], rtol=1e-13, atol=1e-13)
+    assert np.allclose(O, Os, rtol=1e-12, atol=1e-14)
+
+
+def test_negative_window_is_rejected():
+    x = mi.make_inputs(1, 1, 2, mi.BF16, ("list", [10]), page_size=16, seed=29)
+    with pytest.raises(ValueError):
+        _run(x, window=-1)
 
 
 # ---------------------------------------------------------------- invariants
