@@ -143,7 +143,14 @@ typedef struct mla_options {
   int32_t stages;       /* 0: both kernels; 1: only the split-KV kernel; 2: only the merge kernel
                            (re-merging the partials a previous call with the same arguments left in
                            the workspace).  1 and 2 exist to time each kernel back to back. */
-  int32_t reserved[4];
+  int32_t window;       /* > 0: sliding-window mask.  Token t of a sequence sees only its last
+                           `window` visible keys, [max(0, n_t - window), n_t) with
+                           n_t = clamp(L - q_len + t + 1, 0, L); tiles before the earliest
+                           such key are never read.  0: the plain causal mask.  (TokenSpeed
+                           MLA article, section 6: a sliding-window mask among the decode
+                           tests; the convention is this library's reading.)  < 0:
+                           MLA_ERR_SHAPE.  Plan the workspace with the same options. */
+  int32_t reserved[3];
   void* split_event;    /* hipEvent_t or NULL: recorded on `stream` after the split-KV kernel
                            and before the merge kernel, so callers can time each kernel */
 } mla_options;

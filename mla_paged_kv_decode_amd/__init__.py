@@ -46,18 +46,21 @@ class MlaShape(ctypes.Structure):
 
 class MlaOptions(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int32), ("no_fold", ctypes.c_int32), ("partial_fp32", ctypes.c_int32),
-                ("stages", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4), ("split_event", ctypes.c_void_p)]
+                ("stages", ctypes.c_int32), ("window", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
+                ("split_event", ctypes.c_void_p)]
 
 
 def options(num_splits: int = 0, no_fold: bool = False, partial_fp32: bool = False, split_event=None,
-            stages: int = 0) -> MlaOptions:
+            stages: int = 0, window: int = 0) -> MlaOptions:
     """mla_options; split_event is a raw hipEvent_t (e.g. torch.cuda.Event().cuda_event after one record);
-    stages 1 / 2 launch only the split-KV / only the merge kernel."""
+    stages 1 / 2 launch only the split-KV / only the merge kernel; window > 0 is the sliding-window mask
+    (token t sees keys [max(0, n_t - window), n_t))."""
     o = MlaOptions()
     o.num_splits = int(num_splits)
     o.no_fold = int(bool(no_fold))
     o.partial_fp32 = int(bool(partial_fp32))
     o.stages = int(stages)
+    o.window = int(window)
     o.split_event = split_event
     return o
 

@@ -66,7 +66,12 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int num_cus, const mla_
   pl.m_tiles = (pl.H_eff + mla::kTileM - 1) / mla::kTileM;
   pl.U = pl.q_len_eff * pl.m_tiles;
   pl.part_bf16 = (opt && opt->partial_fp32) ? 0 : 1;
-  const long long units_per_seq = max_seq_len > 0 ? (max_seq_len + mla::kUnitKeys - 1) / mla::kUnitKeys : 1;
+  long long units_per_seq = max_seq_len > 0 ? (max_seq_len + mla::kUnitKeys - 1) / mla::kUnitKeys : 1;
+  if (opt && opt->window > 0) {
+    // a window reads at most window + q_len - 1 keys per sequence, from a unit-aligned start
+    const long long w_units = ((long long)opt->window + q_len - 1 + mla::kUnitKeys - 1) / mla::kUnitKeys + 1;
+    if (w_units < units_per_seq) units_per_seq = w_units;
+  }
   const long long units_max = (long long)B * units_per_seq;
   int G;
   if (opt && opt->num_splits > 0) {
@@ -98,7 +103,7 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int num_cus, const mla_
 
 std::mutex g_mu;
 std::map<int, int> g_cus;  // device -> compute units (0 = not gfx950)
-std::map<std::tuple<int, int, int, int, int, int, int, int, int>, Plan> g_plans;
+std::map<std::tuple<int, int, int, int, int, int, int, int, int, int>, Plan> g_plans;
 
 int device_cus(int* dev_out, int* cus_out) {
   int dev = 0;
@@ -140,7 +145,7 @@ int check_plan_args(int B, int q_len, int H, int max_seq_len) {
 
 int cached_plan(int dev, int cus, int B, int q_len, int H, int max_seq_len, const mla_options* opt, Plan* out) {
   const auto key = std::make_tuple(dev, B, q_len, H, max_seq_len, opt ? opt->num_splits : 0, opt ? opt->no_fold : 0,
-                                   opt ? opt->partial_fp32 : 0, cus);
+                                   opt ? opt->partial_fp32 : 0, cus, opt ? opt->window : 0);
   std::lock_guard<std::mutex> lk(g_mu);
   auto it = g_plans.find(key);
   if (it == g_plans.end()) it = g_plans.emplace(key, make_plan(B, q_len, H, max_seq_len, cus, opt)).first;
@@ -154,6 +159,7 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
                 float softmax_scale, float q_scale, float kv_scale, void* out, float* lse, void* ws, size_t ws_bytes,
                 void* stream, const mla_options* opt) {
   if (opt && (opt->stages < 0 || opt->stages > 2)) return fail(MLA_ERR_SHAPE, "options.stages must be 0, 1 or 2");
+  if (opt && opt->window < 0) return fail(MLA_ERR_SHAPE, "options.window must be >= 0 (got %d)", opt->window);
   if (!s) return fail(MLA_ERR_NULL, "shape is NULL");
   if (s->dtype == MLA_DTYPE_FP16) return fail(MLA_ERR_UNSUPPORTED, "fp16 inputs are not supported");
   if (s->dtype != MLA_DTYPE_BF16 && s->dtype != MLA_DTYPE_FP8_E4M3)
@@ -224,6 +230,7 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
   p.s_scale_log2 = (float)((double)softmax_scale * (double)q_scale * (double)kv_scale * 1.4426950408889634074);
   p.v_scale = kv_scale;
   p.part_bf16 = pl.part_bf16;
+  p.window = opt ? opt->window : 0;
   const int tile = dt == mla::kFp8 ? 64 : 32;
   hipStream_t st = (hipStream_t)stream;
   const int stages = opt ? opt->stages : 0;
@@ -262,6 +269,7 @@ int mla_plan_for_cus(int32_t batch, int32_t q_len, int32_t num_heads, int32_t ma
   if (!num_splits || !workspace_bytes || !fold) return fail(MLA_ERR_NULL, "output pointers must be non-NULL");
   int rc = check_plan_args(batch, q_len, num_heads, max_seq_len);
   if (rc) return rc;
+  if (options && options->window < 0) return fail(MLA_ERR_SHAPE, "options.window must be >= 0 (got %d)", options->window);
   if (num_cus < 1) return fail(MLA_ERR_SHAPE, "num_cus must be >= 1");
   const Plan pl = make_plan(batch, q_len, num_heads, max_seq_len, num_cus, options);
   *num_splits = pl.G;
@@ -275,6 +283,7 @@ int mla_workspace_bytes_ex(int32_t batch, int32_t q_len, int32_t num_heads, int3
   if (!num_splits || !workspace_bytes) return fail(MLA_ERR_NULL, "output pointers must be non-NULL");
   int rc = check_plan_args(batch, q_len, num_heads, max_seq_len);
   if (rc) return rc;
+  if (options && options->window < 0) return fail(MLA_ERR_SHAPE, "options.window must be >= 0 (got %d)", options->window);
   int dev = 0, cus = 0;
   rc = device_cus(&dev, &cus);
   if (rc) return rc;

@@ -35,6 +35,7 @@ struct PartialParams {
   float s_scale_log2;        // softmax_scale * q_scale * kv_scale * log2(e)
   float v_scale;             // kv_scale (V dequantisation)
   int32_t part_bf16;
+  int32_t window;            // sliding window in keys (0: none)
 };
 
 struct CombineParams {

@@ -188,6 +188,18 @@ __device__ __forceinline__ float xor32_sum(float x) {
 __device__ __forceinline__ void pin_agpr(v16f& x) { asm volatile("" : "+a"(x)); }
 
 __device__ __forceinline__ int units_of(int L) { return L > 0 ? (L >> 6) + ((L & 63) != 0) : 1; }
+// First key any query token of a sequence of length L can see, rounded down
+// to a 64-key unit: 0 without a sliding window, else the earliest window start
+// (token 0's, n_0 - window) rounded down.  The sequence's work is the units
+// from there to L; tiles before it are never read.
+__device__ __forceinline__ int seq_key0(int L, int q_len, int window) {
+  if (window <= 0) return 0;
+  const long long lo = (long long)L - q_len + 1 - window;
+  return lo > 0 ? (int)(lo & ~(long long)(kUnitKeys - 1)) : 0;
+}
+__device__ __forceinline__ int seq_units(int L, int q_len, int window) {
+  return units_of(L - seq_key0(L, q_len, window));
+}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -230,7 +242,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // ---------------------------------------------------------------------------
-// Balanced partition of the batch's KV work: sequence b owns units_of(L_b)
+// Balanced partition of the batch's KV work: sequence b owns seq_units(L_b)
 // consecutive 64-key units; slice w of G covers units [w*T/G, (w+1)*T/G).
 // Every (slice, sequence) intersection is one segment; its partial lives in
 // workspace slot w + b (unique along the monotone staircase of segments).
@@ -255,7 +267,7 @@ struct SegmentCtx {
 // result could overflow: the workgroup then recomputes the segment with
 // m_ref set to the exact row maxima seen in the first pass.
 // ---------------------------------------------------------------------------
-template <int DT, bool FAST>
+template <int DT, bool FAST, bool WIN>
 __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem, int* s_flag, const SegmentCtx& sg,
                                             int g, int mt, int wave, int lane) {
   using TR = Traits<DT>;
@@ -276,8 +288,10 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   const int gF = g * p.F;
   // keys visible to the last token of this query group
   const int n_gmax = min(max(L - p.q_len + gF + p.F, 0), L);
-  const int k0 = sg.u0 * kUnitKeys;
-  const int k1 = min(sg.u1 * kUnitKeys, n_gmax);
+  const int window = WIN ? p.window : 0;  // sliding window (kernels built without one fold it away)
+  const int kbase = seq_key0(L, p.q_len, window);  // unit 0 of the sequence starts here
+  const int k0 = kbase + sg.u0 * kUnitKeys;
+  const int k1 = min(kbase + sg.u1 * kUnitKeys, n_gmax);
 
   // this lane's query row (row n of the wave's 32)
   const int r = 32 * wave + n;
@@ -286,7 +300,22 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   const int fold = row_valid ? m / p.H : 0;
   const int t_tok = gF + fold;
   const int n_row = row_valid ? min(max(L - p.q_len + t_tok + 1, 0), L) : 0;
-  const int lim = min(n_row, k1);  // keys [k0, lim) are visible to this row
+  const int lim = min(n_row, k1);  // keys [max(k0, lo), lim) are visible to this row
+  const int lo = window > 0 ? max(n_row - window, 0) : 0;  // sliding-window start
+  // Masking bound of this row, (key - lo) unsigned >= vis for masked keys: below
+  // lo or at/after lim.  With a window it is rebuilt from an opaque copy of
+  // n_row where a tile is masked, so that one value stays live across the loop.
+  auto mask_bounds = [&](int& lo_m, uint32_t& vis_m) {
+    if constexpr (WIN) {
+      int nr = n_row;
+      asm volatile("" : "+v"(nr));
+      lo_m = window > 0 ? max(nr - window, 0) : 0;
+      vis_m = (uint32_t)max(min(nr, k1) - lo_m, 0);
+    } else {
+      lo_m = 0;
+      vis_m = (uint32_t)lim;
+    }
+  };
   const size_t rows_per_b = (size_t)p.q_len * p.H;
   const bool wave_active = (mt * kTileM + 32 * wave) < p.H_eff;
 
@@ -449,10 +478,15 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
       for (int kk = 0; kk < kDmaPerWave; ++kk) dma_issue(kk);
     };
 
-    // smallest visible limit over the wave's rows: tiles below it need no mask
-    int lim_min = lim;
+    // smallest visible limit and largest window start over the wave's rows:
+    // tiles inside [lo_max, lim_min) need no mask
+    int lim_min = lim, lo_max = lo;
 #pragma unroll
-    for (int o2 = 32; o2 > 0; o2 >>= 1) lim_min = min(lim_min, __shfl_xor(lim_min, o2, 64));
+    for (int o2 = 32; o2 > 0; o2 >>= 1) {
+      lim_min = min(lim_min, __shfl_xor(lim_min, o2, 64));
+      lo_max = max(lo_max, __shfl_xor(lo_max, o2, 64));
+    }
+    auto tile_needs_mask = [&](int key0) { return key0 + TILE > lim_min || key0 < lo_max; };
 
     // per-lane LDS read geometry
     int kaddr[4];
@@ -563,11 +597,14 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         auto part_a = [&](int slot, int key0, bool need_mask) {
           if (slot == 0) {
             if (need_mask) {
+              int lo_m;
+              uint32_t vis_m;
+              mask_bounds(lo_m, vis_m);
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                if (key >= lim) s0[r] = -INFINITY;
-                if (key + 32 >= lim) s1[r] = -INFINITY;
+                if ((uint32_t)(key - lo_m) >= vis_m) s0[r] = -INFINITY;
+                if ((uint32_t)(key + 32 - lo_m) >= vis_m) s1[r] = -INFINITY;
               }
             }
             fence_v(s0);
@@ -783,7 +820,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         dma_setup(2);
         qk_chain(stage(0), false);
         {
-          const bool nm = k0 + TILE > lim_min;
+          const bool nm = tile_needs_mask(k0);
 #pragma unroll
           for (int slot = 0; slot < 16; ++slot) part_a(slot, k0, nm);
         }
@@ -797,7 +834,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           pv_prefetch(stage(t - 1));
           lds_barrier();  // P of tile t-1 from all waves is visible
           const int key0 = k0 + t * TILE;
-          pv_chain(stage(t - 1), true, key0, key0 + TILE > lim_min);
+          pv_chain(stage(t - 1), true, key0, tile_needs_mask(key0));
         }
         hb = s1;
 #pragma unroll
@@ -844,10 +881,13 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             mx_raw = -INFINITY;
             lsum = 0.f;
             if (need_mask) {
+              int lo_m;
+              uint32_t vis_m;
+              mask_bounds(lo_m, vis_m);
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 const int key = key0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                if (key >= lim) sc[r] = -INFINITY;
+                if ((uint32_t)(key - lo_m) >= vis_m) sc[r] = -INFINITY;
               }
             }
 #pragma unroll
@@ -897,7 +937,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         v4i pp0 = v4i{0, 0, 0, 0}, pp1 = v4i{0, 0, 0, 0};
         if (wave_active) {
           qk(smem, sc);
-          const bool nm = k0 + TILE > lim_min;
+          const bool nm = tile_needs_mask(k0);
 #pragma unroll
           for (int i = 0; i < 8; ++i) sm_chunk(i, k0, nm);
           pp0 = pb[0];
@@ -911,7 +951,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           const lds_t* stp = smem + ((tt - 1) % kStages) * kStageBytes;
           const int key0 = k0 + tt * TILE;
           qk(st, sc);
-          pv(stp, pp0, pp1, true, key0, key0 + TILE > lim_min);
+          pv(stp, pp0, pp1, true, key0, tile_needs_mask(key0));
           pp0 = pb[0];
           pp1 = pb[1];
         }
@@ -1102,7 +1142,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   }
 }
 
-template <int DT, bool FAST>
+template <int DT, bool FAST, bool WIN>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_split_kv_partial(PartialParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kLdsBytes];
@@ -1135,7 +1175,8 @@ mla_split_kv_partial(PartialParams p) {
   const int kper = (p.B + 63) >> 6;
   const int bl0 = min(lane * kper, p.B), bl1 = min(bl0 + kper, p.B);
   long long own = 0;
-  for (int bb = bl0; bb < bl1; ++bb) own += units_of(p.seq_lens[bb]);
+  const int window = WIN ? p.window : 0;
+  for (int bb = bl0; bb < bl1; ++bb) own += seq_units(p.seq_lens[bb], p.q_len, window);
   const long long incl = wave_incl_scan_ll(own);
   const long long T = readlane_ll(incl, 63);
   // the merge needs T to recognise empty slices (they write no partials)
@@ -1149,7 +1190,7 @@ mla_split_kv_partial(PartialParams p) {
   long long P = readlane_ll(excl, hl);
   int b = hl * kper;
   while (b + 1 < p.B) {
-    const int nb = units_of(seq_lens[b]);
+    const int nb = seq_units(seq_lens[b], p.q_len, window);
     if (t0 < P + nb) break;
     P += nb;
     ++b;
@@ -1158,7 +1199,7 @@ mla_split_kv_partial(PartialParams p) {
   // ---- segments of this slice ----
   long long cur = t0;
   while (cur < t1 && b < p.B) {
-    const int nb = units_of(seq_lens[b]);
+    const int nb = seq_units(seq_lens[b], p.q_len, window);
     const long long seg_end = min(t1, P + nb);
     SegmentCtx sg;
     sg.b = b;
@@ -1170,7 +1211,7 @@ mla_split_kv_partial(PartialParams p) {
       p.meta[2 * b] = w;
       p.meta[2 * b + 1] = slice_of_unit(P + nb - 1, T, p.G);
     }
-    run_segment<DT, FAST>(p, smem, s_flag, sg, g, mt, wave, lane);
+    run_segment<DT, FAST, WIN>(p, smem, s_flag, sg, g, mt, wave, lane);
     cur = seg_end;
     P += nb;
     ++b;
@@ -1403,16 +1444,25 @@ __global__ void __launch_bounds__(256) mla_kv_pack_fp8(PackParams p) {
 
 hipError_t launch_partial(const PartialParams& p, int dtype, bool fast_pages, hipStream_t stream) {
   const dim3 grid((unsigned)(p.G * p.U)), block(kThreads);
+  // kernels without a sliding window are separate instantiations, so the
+  // window's per-row state costs them no registers
+  const bool win = p.window > 0;
   if (dtype == kFp8) {
-    if (fast_pages)
-      hipLaunchKernelGGL((mla_split_kv_partial<kFp8, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((mla_split_kv_partial<kFp8, false>), grid, block, 0, stream, p);
+    if (fast_pages) {
+      if (win) hipLaunchKernelGGL((mla_split_kv_partial<kFp8, true, true>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((mla_split_kv_partial<kFp8, true, false>), grid, block, 0, stream, p);
+    } else {
+      if (win) hipLaunchKernelGGL((mla_split_kv_partial<kFp8, false, true>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((mla_split_kv_partial<kFp8, false, false>), grid, block, 0, stream, p);
+    }
   } else {
-    if (fast_pages)
-      hipLaunchKernelGGL((mla_split_kv_partial<kBf16, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((mla_split_kv_partial<kBf16, false>), grid, block, 0, stream, p);
+    if (fast_pages) {
+      if (win) hipLaunchKernelGGL((mla_split_kv_partial<kBf16, true, true>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((mla_split_kv_partial<kBf16, true, false>), grid, block, 0, stream, p);
+    } else {
+      if (win) hipLaunchKernelGGL((mla_split_kv_partial<kBf16, false, true>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((mla_split_kv_partial<kBf16, false, false>), grid, block, 0, stream, p);
+    }
   }
   return hipGetLastError();
 }

@@ -118,15 +118,17 @@ def test_validation_errors_without_device():
 
 
 def test_options_layout_matches_header():
-    # mla_options: five int32 fields, four reserved int32, then a pointer at byte 32
+    # mla_options: five int32 fields, three reserved int32, then a pointer at byte 32
     o = mla.MlaOptions
-    assert [o.num_splits.offset, o.no_fold.offset, o.partial_fp32.offset, o.stages.offset, o.reserved.offset,
-            o.split_event.offset] == [0, 4, 8, 12, 16, 32]
+    assert [o.num_splits.offset, o.no_fold.offset, o.partial_fp32.offset, o.stages.offset, o.window.offset,
+            o.reserved.offset, o.split_event.offset] == [0, 4, 8, 12, 16, 20, 32]
     assert ctypes.sizeof(o) == 40
     text = open(HEADER).read()
     body = text[text.index("typedef struct mla_options"):text.index("} mla_options;")]
     fields = re.findall(r"(int32_t|void\*)\s+(\w+)(\[\d+\])?;", body)
-    assert [f[1] for f in fields] == ["num_splits", "no_fold", "partial_fp32", "stages", "reserved", "split_event"]
+    assert [f[1] for f in fields] == ["num_splits", "no_fold", "partial_fp32", "stages", "window", "reserved",
+                                      "split_event"]
+    assert re.search(r"int32_t\s+reserved\[3\];", body)
 
 
 def test_stages_option_validated_before_any_device_work():
@@ -138,6 +140,23 @@ def test_stages_option_validated_before_any_device_work():
                              ctypes.byref(opts))
         assert rc == -3
         assert b"stages" in L.mla_last_error()
+
+
+def test_window_option_validated_and_planned():
+    L = mla.lib()
+    shape = _shape()
+    opts = mla.options(window=-5)
+    rc = L.mla_decode_ex(ctypes.byref(shape), 16, 16, 16, 16, 1.0, 1.0, 1.0, 16, 16, None, 0, None,
+                         ctypes.byref(opts))
+    assert rc == -3 and b"window" in L.mla_last_error()
+    with pytest.raises(mla.MlaError):
+        mla.plan_for_cus(4, 4, 32, 81920, 256, mla.options(window=-1))
+    # a window bounds each sequence's work at window + q_len - 1 keys (+ one unit of alignment),
+    # so the planned slice count shrinks with it; a window past every length changes nothing
+    assert mla.plan_for_cus(4, 4, 32, 81920, 256)[0] == 256
+    assert mla.plan_for_cus(4, 4, 32, 81920, 256, mla.options(window=4096))[0] == 64
+    assert mla.plan_for_cus(1, 4, 32, 81920, 256, mla.options(window=128))[0] == 1
+    assert mla.plan_for_cus(4, 4, 32, 8192, 256, mla.options(window=100000)) == mla.plan_for_cus(4, 4, 32, 8192, 256)
 
 
 def test_pack_validation_without_device():

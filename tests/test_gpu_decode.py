@@ -312,3 +312,58 @@ def test_stages_split_then_merge_equals_one_call():
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
+# ---------------------------------------------------------------- sliding window
+# (B, q_len, H, dtype, lens, page_size, window): windows of one key, within a tile, a tile, many
+# tiles; short pages take the kernels for pages below a tile
+WINDOW_CASES = [
+    (2, 4, 32, mi.FP8_E4M3, [2500, 700], 64, 1),
+    (2, 4, 32, mi.BF16, [2500, 700], 64, 37),
+    (3, 4, 16, mi.FP8_E4M3, [90, 1300, 5], 64, 64),
+    (1, 1, 16, mi.BF16, [3000], 64, 500),
+    (2, 4, 8, mi.FP8_E4M3, [1000, 333], 16, 200),
+    (2, 2, 8, mi.BF16, [333, 2], 16, 100),
+]
+
+
+@pytest.mark.parametrize("B,q_len,H,dtype,lens,ps,window", WINDOW_CASES)
+def test_window_parity(B, q_len, H, dtype, lens, ps, window):
+    x = mi.make_inputs(B, q_len, H, dtype, ("list", lens), page_size=ps, seed=200 + B * 3 + H + window)
+    print(f"window={window} B={B} q_len={q_len} H={H} dtype={dtype} lens={lens} ps={ps}", flush=True)
+    out, lse = run_gpu(x, opts=mla.options(window=window))
+    assert_parity(x, out, lse, run_oracle(x, window=window))
+
+
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+@pytest.mark.parametrize("splits", [1, 3, 64])
+def test_window_forced_splits(dtype, splits):
+    x = mi.make_inputs(3, 4, 32, dtype, ("list", [2500, 90, 1300]), seed=211)
+    print(f"window=300 splits={splits} dtype={dtype}", flush=True)
+    out, lse = run_gpu(x, opts=mla.options(window=300, num_splits=splits))
+    assert_parity(x, out, lse, run_oracle(x, window=300))
+
+
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+def test_window_covering_every_key_is_bit_identical(dtype):
+    """A window at least as long as every sequence selects the same keys and the same plan."""
+    x = mi.make_inputs(3, 4, 32, dtype, ("list", [700, 5, 1300]), seed=213)
+    t = to_dev(x)
+    base, lse_b = run_gpu(x, tensors=t)
+    win, lse_w = run_gpu(x, opts=mla.options(window=1300), tensors=t)
+    assert torch.equal(base, win) and torch.equal(lse_b, lse_w)
+
+
+def test_window_full_size_agentic_sampled():
+    """The 80K-key FP8 workload with a 4096-key window: only the window's pages are read; the whole
+    output is checked for structure and one sequence against the oracle."""
+    x = mi.workload_inputs("agentic_b4_q4_h32_fp8_80k")
+    t = to_dev(x)
+    out, lse = run_gpu(x, opts=mla.options(window=4096), tensors=t)
+    O = out_f64(out)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse.cpu().numpy()))
+    sub = mi.DecodeInputs(q=x.q[:1], kv_cache=x.kv_cache, block_table=x.block_table[:1], seq_lens=x.seq_lens[:1],
+                          dtype=x.dtype, q_scale=x.q_scale, kv_scale=x.kv_scale, softmax_scale=x.softmax_scale,
+                          page_size=x.page_size)
+    ref = run_oracle(sub, window=4096)
+    assert_parity(sub, out[:1], lse[:1], ref, flat=True)
