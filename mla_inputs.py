@@ -32,7 +32,9 @@ D_QK = 576
 D_V = 512
 BF16 = 1
 FP8_E4M3 = 2
+FP16 = 3
 NAN_BF16 = 0x7FC0
+NAN_F16 = 0x7E00
 NAN_E4M3 = 0x7F
 
 # The five decode workloads (sizes from the headline benchmark definition).
@@ -87,6 +89,12 @@ def _cast_bf16(x: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
+def _cast_f16(x: np.ndarray) -> np.ndarray:
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+
+
 def _cast_e4m3(x: np.ndarray, scale: float) -> np.ndarray:
     import torch
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)) / np.float32(scale)
@@ -97,6 +105,8 @@ def _cast_e4m3(x: np.ndarray, scale: float) -> np.ndarray:
 def _quantize(x: np.ndarray, dtype: int):
     if dtype == BF16:
         return _cast_bf16(x), 1.0
+    if dtype == FP16:
+        return _cast_f16(x), 1.0
     amax = float(np.max(np.abs(x))) if x.size else 1.0
     scale = amax / 448.0 if amax > 0 else 1.0
     return _cast_e4m3(x, scale), scale
@@ -109,12 +119,13 @@ def _draw_pool(rng, num_pages, page_size, dtype):
     """N(0,1) pool drawn chunk by chunk into a preallocated output (no large temporaries)."""
     shape = (num_pages, page_size, D_QK)
     buf = np.empty((POOL_CHUNK_PAGES, page_size, D_QK), dtype=np.float32)
-    if dtype == BF16:
+    if dtype in (BF16, FP16):
+        cast = _cast_bf16 if dtype == BF16 else _cast_f16
         out = np.empty(shape, dtype=np.uint16)
         for p0 in range(0, num_pages, POOL_CHUNK_PAGES):
             n = min(POOL_CHUNK_PAGES, num_pages - p0)
             rng.standard_normal(out=buf[:n], dtype=np.float32)
-            out[p0:p0 + n] = _cast_bf16(buf[:n])
+            out[p0:p0 + n] = cast(buf[:n])
         return out, 1.0
     state = rng.bit_generator.state
     amax = 0.0
@@ -178,7 +189,7 @@ def make_inputs(B, q_len, H, dtype, lens, *, page_size=64, seed=0, spare_pages=8
     q, q_scale = _quantize(q32, dtype)
     del q32
     kv, kv_scale = _draw_pool(rng, num_pages, page_size, dtype)
-    nan_code = NAN_BF16 if dtype == BF16 else NAN_E4M3
+    nan_code = {BF16: NAN_BF16, FP16: NAN_F16}.get(dtype, NAN_E4M3)
     used = np.zeros(num_pages, dtype=bool)
     for b in range(B):
         used[block_table[b, :int(pages_per_seq[b])]] = True

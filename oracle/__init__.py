@@ -32,6 +32,7 @@ _lib = None
 
 BF16 = 1
 FP8_E4M3 = 2
+FP16 = 3
 D_QK = 576
 D_V = 512
 
@@ -59,6 +60,8 @@ def _load():
     lib.oracle_mla_decode.restype = i
     lib.oracle_dec_bf16.argtypes = [ctypes.c_uint16]
     lib.oracle_dec_bf16.restype = d
+    lib.oracle_dec_f16.argtypes = [ctypes.c_uint16]
+    lib.oracle_dec_f16.restype = d
     lib.oracle_dec_e4m3.argtypes = [ctypes.c_uint8]
     lib.oracle_dec_e4m3.restype = d
     lib.oracle_enc_e4m3.argtypes = [d]
@@ -80,6 +83,12 @@ def dec_bf16(bits) -> np.ndarray:
     lib = _load()
     a = np.asarray(bits, dtype=np.uint16)
     return np.array([lib.oracle_dec_bf16(int(x)) for x in a.ravel()], dtype=np.float64).reshape(a.shape)
+
+
+def f16_table() -> np.ndarray:
+    """All 65536 IEEE binary16 patterns decoded to float64 (index = bit pattern), from the format definition."""
+    lib = _load()
+    return np.array([lib.oracle_dec_f16(h) for h in range(65536)], dtype=np.float64)
 
 
 def e4m3_table() -> np.ndarray:
@@ -110,7 +119,7 @@ def mla_decode(q, kv_cache, block_table, seq_lens, *, dtype: int, softmax_scale:
                num_threads: int = 0, want_absv: bool = False):
     """fp64 MLA decode.
 
-    q: uint16 (bf16 bits) or uint8 (e4m3 codes) array [B, q_len, H, 576].
+    q: uint16 (bf16 or fp16 bits) or uint8 (e4m3 codes) array [B, q_len, H, 576]; dtype BF16, FP16 or FP8_E4M3.
     kv_cache: same dtype, [num_pages, page_size, 576].
     block_table: int32 [B, max_pages]; seq_lens: int32 [B].
     Returns (O float64 [B, q_len, H, 512], LSE float64 [B, q_len, H]).
@@ -124,9 +133,9 @@ def mla_decode(q, kv_cache, block_table, seq_lens, *, dtype: int, softmax_scale:
     kv_cache = np.ascontiguousarray(kv_cache)
     block_table = np.ascontiguousarray(block_table, dtype=np.int32)
     seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
-    want = np.uint16 if dtype == BF16 else np.uint8
+    want = np.uint8 if dtype == FP8_E4M3 else np.uint16
     if q.dtype != want or kv_cache.dtype != want:
-        raise TypeError("q and kv_cache must hold raw bf16 bits (uint16) or e4m3 codes (uint8)")
+        raise TypeError("q and kv_cache must hold raw bf16 / fp16 bits (uint16) or e4m3 codes (uint8)")
     B, q_len, H, dq = q.shape
     num_pages, page_size, dk = kv_cache.shape
     if dq != D_QK or dk != D_QK:

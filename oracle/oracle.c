@@ -48,13 +48,26 @@
 #define ORC_D_QK 576
 #define ORC_D_V 512
 
-enum { ORC_BF16 = 1, ORC_FP8_E4M3 = 2 };
+enum { ORC_BF16 = 1, ORC_FP8_E4M3 = 2, ORC_FP16 = 3 };
 
 double oracle_dec_bf16(uint16_t bits) {
   uint32_t u = (uint32_t)bits << 16;
   float f;
   memcpy(&f, &u, 4);
   return (double)f;
+}
+
+/* IEEE binary16: bias 15, 10 fraction bits, subnormals m/1024 * 2^-14, exponent 31 = inf/NaN
+ * (tokenspeed-mla package page: FP16 is one of the decode input types). */
+double oracle_dec_f16(uint16_t h) {
+  int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double v;
+  if (e == 31) return m ? NAN : (s ? -INFINITY : INFINITY);
+  if (e == 0)
+    v = ldexp((double)m / 1024.0, -14);
+  else
+    v = ldexp(1.0 + (double)m / 1024.0, e - 15);
+  return s ? -v : v;
 }
 
 double oracle_dec_e4m3(uint8_t c) {
@@ -72,6 +85,9 @@ static void decode_row(const void* base, int dtype, size_t elem_index, int n, do
   if (dtype == ORC_BF16) {
     const uint16_t* p = (const uint16_t*)base + elem_index;
     for (int d = 0; d < n; ++d) dst[d] = scale * oracle_dec_bf16(p[d]);
+  } else if (dtype == ORC_FP16) {
+    const uint16_t* p = (const uint16_t*)base + elem_index;
+    for (int d = 0; d < n; ++d) dst[d] = scale * oracle_dec_f16(p[d]);
   } else {
     const uint8_t* p = (const uint8_t*)base + elem_index;
     for (int d = 0; d < n; ++d) dst[d] = scale * oracle_dec_e4m3(p[d]);
@@ -153,7 +169,7 @@ int oracle_mla_decode(const void* q, const void* kv, int dtype, const int32_t* b
                       double softmax_scale, double q_scale, double kv_scale, int split_len, int window,
                       double* out, double* lse, double* absv, int num_threads) {
   if (!q || !kv || !block_table || !seq_lens || !out || !lse) return -2;
-  if (dtype != ORC_BF16 && dtype != ORC_FP8_E4M3) return -2;
+  if (dtype != ORC_BF16 && dtype != ORC_FP8_E4M3 && dtype != ORC_FP16) return -2;
   if (B < 0 || q_len <= 0 || H <= 0 || page_size <= 0 || max_pages < 0 || split_len < 0 || window < 0) return -2;
   if (absv && split_len > 0) return -2;
   for (int b = 0; b < B; ++b) {

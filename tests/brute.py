@@ -16,6 +16,8 @@ def decode_values(raw: np.ndarray, dtype: int) -> np.ndarray:
     t = torch.from_numpy(np.ascontiguousarray(raw))
     if dtype == mi.BF16:
         return t.view(torch.bfloat16).to(torch.float64).numpy()
+    if dtype == mi.FP16:
+        return t.view(torch.float16).to(torch.float64).numpy()
     return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
 
 

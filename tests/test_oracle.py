@@ -50,6 +50,17 @@ def test_bf16_decode_matches_torch():
     assert np.array_equal(ref[fin], got[fin])
 
 
+def test_f16_table_matches_numpy():
+    # every binary16 pattern, including subnormals, infinities and NaNs
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = oracle.f16_table()
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ref[fin], got[fin])
+    assert got[0x3C00] == 1.0 and got[0x0001] == 2.0 ** -24 and got[0x7BFF] == 65504.0 and np.isinf(got[0x7C00])
+
+
 def test_e4m3_encoder_matches_torch_rne():
     table = oracle.e4m3_table()
     finite = [c for c in range(256) if not math.isnan(table[c])]
@@ -91,6 +102,7 @@ def test_fold_factor_worked_example():
 SHAPES = [
     # B, q_len, H, dtype, lens, page_size
     (1, 1, 4, mi.BF16, [5], 16),
+    (2, 4, 3, mi.FP16, [3, 150], 16),
     (2, 4, 8, mi.FP8_E4M3, [3, 200], 16),
     (3, 4, 2, mi.BF16, [0, 4, 300], 64),
     (2, 3, 5, mi.FP8_E4M3, [1, 130], 64),
@@ -170,6 +182,7 @@ WINDOW_SHAPES = [
     (2, 3, 5, mi.FP8_E4M3, [1, 130], 64, 64),
     (1, 2, 8, mi.BF16, [257], 16, 100),
     (2, 1, 3, mi.FP8_E4M3, [40, 77], 16, 1000),
+    (2, 4, 3, mi.FP16, [90, 7], 16, 30),
 ]
 
 
