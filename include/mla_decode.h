@@ -59,7 +59,7 @@ typedef enum mla_status {
   MLA_ERR_SHAPE = -3,       /* a size is out of range or inconsistent */
   MLA_ERR_ALIGN = -4,       /* a device pointer is not aligned as required */
   MLA_ERR_WORKSPACE = -5,   /* workspace NULL, too small, misaligned, or planned for another shape */
-  MLA_ERR_UNSUPPORTED = -6, /* valid but not implemented (e.g. fp16) */
+  MLA_ERR_UNSUPPORTED = -6, /* valid but not implemented */
   MLA_ERR_HIP = -7,         /* a HIP runtime call failed (message names it) */
   MLA_ERR_DEVICE = -8       /* no usable HIP device */
 } mla_status;
@@ -67,7 +67,7 @@ typedef enum mla_status {
 typedef enum mla_dtype {
   MLA_DTYPE_BF16 = 1,     /* bfloat16, stored as 16-bit patterns */
   MLA_DTYPE_FP8_E4M3 = 2, /* OCP FP8 E4M3 (e4m3fn): bias 7, no inf, S.1111.111 = NaN, max 448 */
-  MLA_DTYPE_FP16 = 3      /* reserved: returns MLA_ERR_UNSUPPORTED */
+  MLA_DTYPE_FP16 = 3      /* IEEE binary16 (tokenspeed-mla package page: FP16 / BF16 / FP8 decode inputs) */
 } mla_dtype;
 
 /* Sizes of one decode call.  All fields are element counts. */
@@ -118,7 +118,7 @@ int mla_get_split_kv_and_workspace(int32_t batch, int32_t q_len, int32_t num_hea
  *               max_seq_len are still computed correctly (less balanced).
  *   softmax_scale, q_scale, kv_scale
  *               host floats; dequantised value = stored value * scale (pass
- *               1.0 for bf16 data).
+ *               1.0 for bf16 and fp16 data).
  *   out         device bf16 [batch, q_len, num_heads, 512], contiguous, 16-byte aligned.
  *   lse         device fp32 [batch, q_len, num_heads] or NULL to skip.
  *   workspace   device scratch of workspace_bytes bytes, 256-byte aligned, at
@@ -127,8 +127,7 @@ int mla_get_split_kv_and_workspace(int32_t batch, int32_t q_len, int32_t num_hea
  *               size is 0.  Its contents need no initialisation.
  *   stream      hipStream_t or NULL.
  *
- * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_DTYPE, MLA_ERR_UNSUPPORTED
- * (fp16), MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_DEVICE, MLA_ERR_HIP
+ * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_DTYPE, MLA_ERR_ALIGN, MLA_ERR_WORKSPACE, MLA_ERR_DEVICE, MLA_ERR_HIP
  * (kernel launch failed).  batch == 0 returns MLA_OK and enqueues nothing.
  */
 int mla_decode(const mla_shape* shape, const void* q, const void* kv_cache, const int32_t* block_table,

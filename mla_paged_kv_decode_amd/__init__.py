@@ -172,7 +172,7 @@ def decode(q, kv_cache, block_table, seq_lens, softmax_scale: float, q_scale: fl
            opts: MlaOptions | None = None, stream=None):
     """MLA decode through the C ABI.  Tensors live on the current HIP device.
 
-    q: [B, q_len, H, 576] bfloat16 or float8_e4m3fn; kv_cache: [num_pages,
+    q: [B, q_len, H, 576] bfloat16, float16 or float8_e4m3fn; kv_cache: [num_pages,
     page_size, 576] of the same dtype; block_table: int32 [B, max_pages];
     seq_lens: int32 [B].  Returns (out bf16 [B, q_len, H, 512], lse fp32
     [B, q_len, H] or None).  max_seq_len defaults to max(seq_lens), which

@@ -161,9 +161,8 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
   if (opt && (opt->stages < 0 || opt->stages > 2)) return fail(MLA_ERR_SHAPE, "options.stages must be 0, 1 or 2");
   if (opt && opt->window < 0) return fail(MLA_ERR_SHAPE, "options.window must be >= 0 (got %d)", opt->window);
   if (!s) return fail(MLA_ERR_NULL, "shape is NULL");
-  if (s->dtype == MLA_DTYPE_FP16) return fail(MLA_ERR_UNSUPPORTED, "fp16 inputs are not supported");
-  if (s->dtype != MLA_DTYPE_BF16 && s->dtype != MLA_DTYPE_FP8_E4M3)
-    return fail(MLA_ERR_DTYPE, "dtype %d is not MLA_DTYPE_BF16 or MLA_DTYPE_FP8_E4M3", s->dtype);
+  if (s->dtype != MLA_DTYPE_BF16 && s->dtype != MLA_DTYPE_FP8_E4M3 && s->dtype != MLA_DTYPE_FP16)
+    return fail(MLA_ERR_DTYPE, "dtype %d is not MLA_DTYPE_BF16, MLA_DTYPE_FP16 or MLA_DTYPE_FP8_E4M3", s->dtype);
   int rc = check_plan_args(s->batch, s->q_len, s->num_heads, s->max_seq_len);
   if (rc) return rc;
   if (s->num_pages < 1) return fail(MLA_ERR_SHAPE, "num_pages must be >= 1 (got %d)", s->num_pages);
@@ -199,7 +198,7 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
                   pl.bytes);
   }
 
-  const int dt = s->dtype == MLA_DTYPE_FP8_E4M3 ? mla::kFp8 : mla::kBf16;
+  const int dt = s->dtype == MLA_DTYPE_FP8_E4M3 ? mla::kFp8 : s->dtype == MLA_DTYPE_FP16 ? mla::kFp16 : mla::kBf16;
   int shift = 0;
   while ((1 << shift) < s->page_size) ++shift;
   mla::PartialParams p{};

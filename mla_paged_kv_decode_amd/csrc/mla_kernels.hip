@@ -30,6 +30,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) uint8_t lds_t;
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __attribute__((address_space(3))) v4i lds_v4i;
@@ -37,6 +38,9 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 typedef __attribute__((address_space(4))) const int32_t cint_t;
 
 constexpr float kTau = 32.0f;  // rescale the accumulators only when a row max grows by more (log2 units)
+// fp16 P must stay below 65504, so its rows are recomputed once their max grows by more than 2^15
+template <int DT>
+constexpr float kTauOf = DT == kFp16 ? 15.0f : kTau;
 constexpr float kLn2 = 0.693147180559945309417f;
 constexpr int kDmaPerWave = kStageBytes / 1024 / 4;  // 9 one-KiB LDS writes per wave per tile
 // Epilogue staging: per wave 32 rows of 256 columns; row pitches padded by 8
@@ -75,6 +79,8 @@ struct Traits<kBf16> {
   static constexpr int kRowBytes = 1152;
   static constexpr int kChunks = 72;
 };
+template <>
+struct Traits<kFp16> : Traits<kBf16> {};  // same 2-byte rows and tiles
 
 // LDS layout of a tile: row r, 16-byte chunk c lives at chunk slot
 // r * kChunks + (c ^ swz(r)).  The XOR keeps every access pattern of the
@@ -155,13 +161,24 @@ __device__ __forceinline__ void qk_mfma_f8_first(v16f& acc, const v8i& a, const 
                : "=&v"(acc)
                : "v"(a), "v"(b), "v"(127));
 }
-__device__ __forceinline__ void qk_mfma_bf16(v16f& acc, const v4i& a, const v4i& b, bool last) {
-  if (last) {
-    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+v"(acc)
-                 : "v"(a), "v"(b));
+template <int DT>
+__device__ __forceinline__ void qk_mfma_h16(v16f& acc, const v4i& a, const v4i& b, bool last) {
+  if constexpr (DT == kFp16) {
+    if (last) {
+      asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                   : "+v"(acc)
+                   : "v"(a), "v"(b));
+    } else {
+      asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+    }
   } else {
-    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+    if (last) {
+      asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                   : "+v"(acc)
+                   : "v"(a), "v"(b));
+    } else {
+      asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+    }
   }
 }
 // Scheduling fences.  The instruction selector places pure arithmetic next to
@@ -236,6 +253,27 @@ __device__ __forceinline__ long long readlane_ll(long long v, int l) {
   return (long long)(((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
+// two probabilities in the PV operand format (bf16 or fp16, round to nearest even)
+template <int DT>
+__device__ __forceinline__ uint32_t pack_p16x2(float a, float b) {
+  if constexpr (DT == kFp16) {
+    const _Float16 x = (_Float16)a, y = (_Float16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  } else {
+    const __bf16 x = (__bf16)a, y = (__bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  }
+}
+template <int DT>
+__device__ __forceinline__ v16f pv_mfma_h16(const v4i& v, const v4i& pw, const v16f& acc) {
+  if constexpr (DT == kFp16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, v), __builtin_bit_cast(v8h, pw), acc, 0, 0,
+                                                  0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, v), __builtin_bit_cast(v8bf, pw), acc, 0,
+                                                   0, 0);
+  }
+}
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   __bf16 x = (__bf16)a, y = (__bf16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
@@ -263,7 +301,7 @@ struct SegmentCtx {
 // Softmax bookkeeping: each row's probabilities are taken relative to a
 // reference m_ref fixed at the row's first tile with a visible key, so the
 // output accumulators are only ever touched by MFMA (no rescale in the loop).
-// If a later tile's row max exceeds m_ref by more than kTau (log2 units), the
+// If a later tile's row max exceeds m_ref by more than kTauOf<DT> (log2 units), the
 // result could overflow: the workgroup then recomputes the segment with
 // m_ref set to the exact row maxima seen in the first pass.
 // ---------------------------------------------------------------------------
@@ -325,7 +363,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   // bf16 Q (twice the bytes: the whole ring) is loaded here.
   constexpr int QSTEPS = (DT == kFp8) ? 9 : 36;
   v8i qreg[QSTEPS];
-  if constexpr (DT == kBf16) {
+  if constexpr (DT != kFp8) {
     const size_t qrow_idx = ((size_t)sg.b * p.q_len + gF) * p.H + (size_t)(row_valid ? m : 0);
     const uint8_t* qrow = p.q + qrow_idx * kDqk * ESZ;
     const int keep = row_valid ? -1 : 0;
@@ -504,7 +542,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
       vaddr[1] = kbase * RB + (((2 + dsub) ^ s8) * 16) + 8 * c8;
       vaddr[2] = vaddr[3] = 0;
     } else {
-      const int sw = swz<kBf16>(n);
+      const int sw = swz<DT>(n);
 #pragma unroll
       for (int x = 0; x < 4; ++x) kaddr[x] = n * RB + (((2 * x + hh) ^ sw) * 16);
       const int grp = lane >> 4, hs = grp >> 1, dsub = grp & 1, uu = lane & 15, rr = uu >> 2, c4 = uu & 3;
@@ -867,7 +905,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             v4i an = a;
             if (c + 1 < 36) an = kread(st, c + 1);
             const v4i qb = v4i{qreg[c][0], qreg[c][1], qreg[c][2], qreg[c][3]};
-            qk_mfma_bf16(s, a, qb, c == 35);
+            qk_mfma_h16<DT>(s, a, qb, c == 35);
             __builtin_amdgcn_sched_barrier(0);
             a = an;
           }
@@ -897,7 +935,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             const float rm = fmaxf(mx, __shfl_xor(mx, 32, 64));
             m_seen = fmaxf(m_seen, rm);
             if (m_ref == -INFINITY) m_ref = rm;
-            ovf = ovf || (rm > m_ref + kTau);
+            ovf = ovf || (rm > m_ref + kTauOf<DT>);
             mref = m_ref > -INFINITY ? m_ref : 0.f;
           } else if (i >= 2 && i < 6) {
             const int g4 = i - 2;
@@ -908,13 +946,14 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             }
           } else if (i == 6 || i == 7) {
             const int u = i - 6;
-            pb[u] = v4i{(int)pack_bf16x2(pvv[8 * u + 0], pvv[8 * u + 1]), (int)pack_bf16x2(pvv[8 * u + 2], pvv[8 * u + 3]),
-                        (int)pack_bf16x2(pvv[8 * u + 4], pvv[8 * u + 5]), (int)pack_bf16x2(pvv[8 * u + 6], pvv[8 * u + 7])};
+            pb[u] = v4i{(int)pack_p16x2<DT>(pvv[8 * u + 0], pvv[8 * u + 1]),
+                        (int)pack_p16x2<DT>(pvv[8 * u + 2], pvv[8 * u + 3]),
+                        (int)pack_p16x2<DT>(pvv[8 * u + 4], pvv[8 * u + 5]),
+                        (int)pack_p16x2<DT>(pvv[8 * u + 6], pvv[8 * u + 7])};
             if (u == 1) l_acc += lsum;
           }
         };
         auto pv = [&](const lds_t* st, const v4i& p0, const v4i& p1, bool with_sm, int key0, bool need_mask) {
-          const v8bf pbf0 = __builtin_bit_cast(v8bf, p0), pbf1 = __builtin_bit_cast(v8bf, p1);
           v4i vt0 = vread(st, 0, 0), vt1 = vread(st, 0, 1);
 #pragma unroll
           for (int db = 0; db < 16; ++db) {
@@ -923,8 +962,8 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
               vn0 = vread(st, db + 1, 0);
               vn1 = vread(st, db + 1, 1);
             }
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, vt0), pbf0, o[db], 0, 0, 0);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, vt1), pbf1, o[db], 0, 0, 0);
+            o[db] = pv_mfma_h16<DT>(vt0, p0, o[db]);
+            o[db] = pv_mfma_h16<DT>(vt1, p1, o[db]);
             if (with_sm && db < 8) sm_chunk(db, key0, need_mask);
             __builtin_amdgcn_sched_barrier(0);
             vt0 = vn0;
@@ -1454,6 +1493,14 @@ hipError_t launch_partial(const PartialParams& p, int dtype, bool fast_pages, hi
     } else {
       if (win) hipLaunchKernelGGL((mla_split_kv_partial<kFp8, false, true>), grid, block, 0, stream, p);
       else hipLaunchKernelGGL((mla_split_kv_partial<kFp8, false, false>), grid, block, 0, stream, p);
+    }
+  } else if (dtype == kFp16) {
+    if (fast_pages) {
+      if (win) hipLaunchKernelGGL((mla_split_kv_partial<kFp16, true, true>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((mla_split_kv_partial<kFp16, true, false>), grid, block, 0, stream, p);
+    } else {
+      if (win) hipLaunchKernelGGL((mla_split_kv_partial<kFp16, false, true>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((mla_split_kv_partial<kFp16, false, false>), grid, block, 0, stream, p);
     }
   } else {
     if (fast_pages) {

@@ -100,7 +100,7 @@ def _decode_raw(shape, q=16, kv=16, bt=16, sl=16, out=16, lse=None, ws=None, wsb
 def test_validation_errors_without_device():
     assert _decode_raw(None) == -1
     assert _decode_raw(_shape(dtype=7)) == -2
-    assert _decode_raw(_shape(dtype=mla.DTYPE_FP16)) == -6
+    assert _decode_raw(_shape(dtype=mla.DTYPE_FP16), kv=24) == -4  # fp16 is accepted, then validated
     assert _decode_raw(_shape(page_size=48)) == -3
     assert _decode_raw(_shape(page_size=8)) == -3
     assert _decode_raw(_shape(q_len=0)) == -3

@@ -367,3 +367,38 @@ def test_window_full_size_agentic_sampled():
                           page_size=x.page_size)
     ref = run_oracle(sub, window=4096)
     assert_parity(sub, out[:1], lse[:1], ref, flat=True)
+
+
+# ---------------------------------------------------------------- fp16 inputs
+FP16_CASES = [
+    # B, q_len, H, lens, page_size, options
+    (3, 4, 32, [0, 77, 1000], 64, {}),
+    (2, 1, 128, [4096, 300], 64, {}),
+    (2, 4, 64, [1500, 3], 64, {"num_splits": 3}),
+    (4, 2, 16, [1, 2, 3, 130], 16, {}),
+    (3, 4, 32, [2500, 90, 1300], 64, {"num_splits": 64}),
+    (2, 4, 32, [2500, 700], 64, {"window": 37}),
+]
+
+
+@pytest.mark.parametrize("B,q_len,H,lens,ps,kw", FP16_CASES)
+def test_fp16_parity(B, q_len, H, lens, ps, kw):
+    x = mi.make_inputs(B, q_len, H, mi.FP16, ("list", lens), page_size=ps, seed=300 + B * 5 + H + ps)
+    print(f"fp16 B={B} q_len={q_len} H={H} lens={lens} ps={ps} {kw}", flush=True)
+    out, lse = run_gpu(x, opts=mla.options(**kw) if kw else None)
+    # the derived element-wise bound, as for the bf16 cases (the flat bars are the workloads')
+    assert_parity(x, out, lse, run_oracle(x, window=kw.get("window", 0)))
+
+
+def test_fp16_large_score_growth_is_recomputed():
+    """Scores that grow by far more than fp16's range after the first tile force the row's
+    recomputation with the true maximum; the result must still match the oracle."""
+    x = mi.make_inputs(1, 1, 16, mi.FP16, ("list", [640]), page_size=64, seed=311)
+    kv = x.kv_cache.view(np.float16).astype(np.float32)
+    # the last page's keys get a large component along the queries' dimension 0
+    last = x.block_table[0, 9]
+    kv[last, :, 0] = 60.0
+    x.q.view(np.float16)[0, 0, :, 0] = np.float16(8.0)
+    x.kv_cache[:] = kv.astype(np.float16).view(np.uint16)
+    out, lse = run_gpu(x)
+    assert_parity(x, out, lse, run_oracle(x))
