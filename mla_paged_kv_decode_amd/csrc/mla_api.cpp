@@ -33,7 +33,11 @@ int ok() {
   return MLA_OK;
 }
 
-constexpr int kMinUnitsPerSlice = 4;  // at least 256 keys of work per KV slice
+// At least one 64-key unit per KV slice.  A workgroup's fixed latency chain
+// (sequence lengths, block table, first tiles, epilogue) is about 12 us, so a
+// small batch is faster spread one unit per slice plus the merge (256 keys of
+// bf16: 22 us) than run as fewer, longer slices (28 us as one slice).
+constexpr int kMinUnitsPerSlice = 1;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
