@@ -279,6 +279,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
+// Epilogue stores: the final O of a sequence held by one slice goes out
+// non-temporal (no dirty lines left for the kernel-end writeback); a split
+// partial uses an ordinary store, so the merge that follows finds it in cache.
+__device__ __forceinline__ void store_out(const v4i& v, v4i* dst, bool final_out) {
+  if (final_out) {
+    __builtin_nontemporal_store(v, dst);
+  } else {
+    *dst = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Balanced partition of the batch's KV work: sequence b owns seq_units(L_b)
 // consecutive 64-key units; slice w of G covers units [w*T/G, (w+1)*T/G).
@@ -1010,9 +1021,8 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   if constexpr (DT == kFp8) {
     // Wave w holds O^T for latent dims [128w, 128w+128) of all 128 rows; the
     // row owners publish 1/l, then the whole 128x512 tile is staged in LDS and
-    // written row-contiguous (whole 128-byte lines per store).  The stores are
-    // non-temporal: left dirty in L2 they would be written back at kernel end,
-    // delaying the merge kernel's start.
+    // written row-contiguous (whole 128-byte lines per store; see store_out for
+    // the cache policy of final outputs and partials).
     asm volatile("" : "+v"(lane));
     const int ne = lane & 31, he = lane >> 5;
     const float l_tot = xor32_sum(l_acc);
@@ -1055,7 +1065,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         const int m_r = row0 + row;
         if (m_r < p.H_eff) {
           const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
-          __builtin_nontemporal_store(v, (v4i*)(dst + rowb * kDv + 8 * lane));
+          store_out(v, (v4i*)(dst + rowb * kDv + 8 * lane), sg.single);
         }
       }
     } else {
@@ -1086,7 +1096,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           const int m_r = row0 + row;
           if (m_r < p.H_eff) {
             const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
-            __builtin_nontemporal_store(v, (v4f*)(dst + rowb * kDv + 256 * h + 4 * lane));
+            *(v4f*)(dst + rowb * kDv + 256 * h + 4 * lane) = v;  // a partial: the merge reads it next
           }
         }
         lds_barrier();
@@ -1140,7 +1150,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         const int m_r = wrow0 + r;
         if (m_r < p.H_eff) {
           const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
-          __builtin_nontemporal_store(v, (v4i*)(dst + rowb * kDv + 256 * pass + 8 * ch));
+          store_out(v, (v4i*)(dst + rowb * kDv + 256 * pass + 8 * ch), sg.single);
         }
       }
     }
@@ -1164,7 +1174,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         const int m_r = wrow0 + r;
         if (m_r < p.H_eff) {
           const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
-          __builtin_nontemporal_store(v, (v4f*)(dst + rowb * kDv + 256 * pass + 4 * lane));
+          *(v4f*)(dst + rowb * kDv + 256 * pass + 4 * lane) = v;  // a partial: the merge reads it next
         }
       }
     }
