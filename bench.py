@@ -245,6 +245,47 @@ def cpu_baseline(x, max_threads: int):
                       f"sequence's keys ({int(lens.sum())} keys), fp64, {dt:.2f} s wall"}
 
 
+def bench_pack(args):
+    """The fused K/V pack + FP8 quantise kernel: T tokens of bf16 latent [512] and rope [64] scattered as
+    E4M3 rows into a shuffled cache of T rows (a paged-cache append), K launches back to back."""
+    import torch
+
+    import mla_paged_kv_decode_amd as mla
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    T = args.pack_tokens
+    g = torch.Generator(device="cpu").manual_seed(7)
+    latent = torch.randn(T, 512, generator=g).to(torch.bfloat16).to(dev)
+    rope = torch.randn(T, 64, generator=g).to(torch.bfloat16).to(dev)
+    slots = torch.randperm(T, generator=g).to(torch.int64).to(dev)
+    out = torch.empty(T, 576, dtype=torch.uint8, device=dev)
+    kv_scale = float(latent.float().abs().max().item()) / 448.0
+
+    def run():
+        mla.kv_pack_quantize_fp8(latent, rope, kv_scale, slot_mapping=slots, out=out)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = T * (512 * 2 + 64 * 2 + 8 + 576)  # read latent, rope, slot; write the row
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"metric": "fused K/V pack + FP8 quantise (paged-cache append)", "value": round(gbs, 1),
+                      "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": round(ms, 5), "higher_is_better": True, "dtype": "bf16->fp8_e4m3",
+                      "data": "synthetic", "config": {"workload": f"kv_pack_{T}_tokens", "tokens": T},
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                   "algorithmic_bytes_per_launch": nbytes}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,6 +298,8 @@ def main():
     ap.add_argument("--partial-fp32", action="store_true", help="keep split partials in fp32 (default bf16)")
     ap.add_argument("--copy-calibration", action="store_true", help="run the counter-calibration copy and exit")
     ap.add_argument("--summarize-profile", metavar="DIR", help="summarise rocprofv3 runs under DIR into profiles/")
+    ap.add_argument("--pack-tokens", type=int, default=0,
+                    help="time the fused K/V pack + FP8 quantise kernel on this many tokens instead of the decode")
     args = ap.parse_args()
     if args.summarize_profile:
         summarize_profile(args.summarize_profile, args.workload)
@@ -268,6 +311,9 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "sequences are independent, see DESIGN.md for how the decode would shard", file=sys.stderr)
         sys.exit(2)
+    if args.pack_tokens > 0:
+        bench_pack(args)
+        return
 
     import numpy as np
     import torch

@@ -1444,49 +1444,52 @@ __global__ void __launch_bounds__(256) mla_combine_rows(CombineParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Pack + quantise: one thread per 8 elements of a 576-wide output row.
+// Pack + quantise: one thread per 16 elements of a 576-wide output row, 36
+// threads per token, 7 tokens per 256-thread workgroup (index math in 32 bits).
 // ---------------------------------------------------------------------------
+constexpr int kPackThreadsPerToken = kDqk / 16;                   // 36
+constexpr int kPackTokensPerBlock = 256 / kPackThreadsPerToken;  // 7
+
 __device__ __forceinline__ float quant_in(uint32_t bits16, float scale) {
   const float x = __builtin_bit_cast(float, bits16 << 16) / scale;
   if (x != x) return x;
   return fminf(fmaxf(x, -448.f), 448.f);
 }
 
+// four inputs -> four E4M3 codes (round to nearest even; NaN -> the canonical 0x7F)
+__device__ __forceinline__ uint32_t pack4_e4m3(const float* f) {
+  int wv = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+  wv = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], wv, true);
+  uint32_t u = (uint32_t)wv;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (f[j] != f[j]) u = (u & ~(0xffu << (8 * j))) | (0x7fu << (8 * j));
+  return u;
+}
+
 __global__ void __launch_bounds__(256) mla_kv_pack_fp8(PackParams p) {
-  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = (long long)p.num_tokens * 72;
-  if (gid >= total) return;
-  const int t = (int)(gid / 72);
-  const int grp = (int)(gid - (long long)t * 72);
+  const int tid = threadIdx.x;
+  const int lt = tid / kPackThreadsPerToken;
+  if (lt >= kPackTokensPerBlock) return;
+  const int grp = tid - lt * kPackThreadsPerToken;  // 16-element group: 0..31 latent, 32..35 rope
+  const long long t = (long long)blockIdx.x * kPackTokensPerBlock + lt;
+  if (t >= p.num_tokens) return;
   long long dst = t;
   if (p.slot_mapping != nullptr) dst = p.slot_mapping[t];
   if (dst < 0 || dst >= p.out_rows) return;
-  uint4 x;
-  if (grp < 64) {
-    x = *(const uint4*)(p.latent + (size_t)t * p.latent_stride + 8 * grp);
-  } else {
-    x = *(const uint4*)(p.rope + (size_t)t * p.rope_stride + 8 * (grp - 64));
-  }
-  const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-  float f[8];
+  const uint16_t* src = grp < 32 ? p.latent + (size_t)t * p.latent_stride + 16 * grp
+                                 : p.rope + (size_t)t * p.rope_stride + 16 * (grp - 32);
+  const uint4 x0 = *(const uint4*)src;
+  const uint4 x1 = *(const uint4*)(src + 8);
+  const uint32_t xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  float f[16];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 8; ++j) {
     f[2 * j] = quant_in(xs[j] & 0xffffu, p.scale);
     f[2 * j + 1] = quant_in(xs[j] >> 16, p.scale);
   }
-  uint32_t outw[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    int wv = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * h + 0], f[4 * h + 1], 0, false);
-    wv = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * h + 2], f[4 * h + 3], wv, true);
-    uint32_t u = (uint32_t)wv;
-    // canonical NaN code 0x7F (the convert may set the sign bit)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (f[4 * h + j] != f[4 * h + j]) u = (u & ~(0xffu << (8 * j))) | (0x7fu << (8 * j));
-    outw[h] = u;
-  }
-  *(uint2*)(p.out + (size_t)dst * kDqk + 8 * grp) = make_uint2(outw[0], outw[1]);
+  *(uint4*)(p.out + (size_t)dst * kDqk + 16 * grp) =
+      make_uint4(pack4_e4m3(f), pack4_e4m3(f + 4), pack4_e4m3(f + 8), pack4_e4m3(f + 12));
 }
 
 }  // namespace
@@ -1537,8 +1540,7 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_pack_fp8(const PackParams& p, hipStream_t stream) {
-  const long long total = (long long)p.num_tokens * 72;
-  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  const dim3 grid((unsigned)((p.num_tokens + kPackTokensPerBlock - 1) / kPackTokensPerBlock)), block(256);
   hipLaunchKernelGGL(mla_kv_pack_fp8, grid, block, 0, stream, p);
   return hipGetLastError();
 }

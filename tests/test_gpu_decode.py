@@ -245,6 +245,26 @@ def test_kv_pack_quantize_bit_exact():
     assert np.array_equal(cache.cpu().numpy(), ref2)
 
 
+@pytest.mark.parametrize("scale", [0.0123, 1.0 / 3.0, 2.0 ** -5])
+def test_kv_pack_quantize_every_bf16_input(scale):
+    """Every bf16 bit pattern (NaNs, infinities, subnormals, ties included) through the pack kernel,
+    bit-exact against the oracle's encoder."""
+    import oracle
+
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    T = -(-65536 // 576)
+    flat = np.zeros(T * 576, dtype=np.uint16)
+    flat[:65536] = bits
+    rows = flat.reshape(T, 576)
+    latent_bits, rope_bits = np.ascontiguousarray(rows[:, :512]), np.ascontiguousarray(rows[:, 512:])
+    ref = oracle.kv_pack_quantize_fp8(latent_bits, rope_bits, scale)
+    latent = torch.from_numpy(latent_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    rope = torch.from_numpy(rope_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    got = mla.kv_pack_quantize_fp8(latent, rope, scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
 def test_packed_cache_feeds_decode():
     """Rows written by the pack kernel into a paged cache decode like the oracle says."""
     import oracle
