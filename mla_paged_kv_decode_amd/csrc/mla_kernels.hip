@@ -782,12 +782,14 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         };
         // O^T += V^T P^T for this wave's 128 latent dims (4 blocks of 32) and all
         // four row blocks: each transposed V read feeds four MFMAs.  Accumulator
-        // o[4j + rr] holds latent block j of row block (wave + rr) & 3, so every
-        // block's MFMAs start with this wave's own rows, whose P is still in
-        // registers, and the other waves' P has a full MFMA to arrive.  The first
-        // V block is read before the P barrier (its stage landed long ago).
+        // o[4j + rr] holds latent block j of row block (wave + rr) & 3 (rr = 0 is
+        // this wave's own rows, whose P is still in registers).  The first two V
+        // blocks are read before the P barrier (their stage landed long ago).
         v8i vb[2];
-        auto pv_prefetch = [&](const lds_t* st) { vb[0] = vread(st, 4 * wave); };
+        auto pv_prefetch = [&](const lds_t* st) {
+          vb[0] = vread(st, 4 * wave);
+          vb[1] = vread(st, 4 * wave + 1);
+        };
         auto stage = [&](int t) -> const lds_t* { return smem + (t % kStages) * kStageBytes; };
         // The segment's last tile was loaded whole: rows past its last key hold
         // whatever follows in the page (possibly NaN).  Their scores are masked,
@@ -814,18 +816,22 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             pt[rr] = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
             psc[rr] = *(const __attribute__((address_space(3))) int*)(smem + kPScaleOffset + 256 * r + 4 * lane);
           }
+          // MFMA order (as 4j + rr): both own-row MFMAs of latent blocks 0 and 1
+          // first, so the other waves' P has two MFMAs to arrive from LDS; V
+          // blocks 0 and 1 were read before the barrier, blocks 2 and 3 are
+          // read into the freed registers four MFMAs before their first use.
+          constexpr int kOrder[16] = {0, 4, 1, 2, 3, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              if (rr == 0 && j + 1 < 4) vb[(j + 1) & 1] = vread(st, 4 * wave + j + 1);
-              fence_v(vb[j & 1]);
-              o[4 * j + rr] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb[j & 1], pt[rr], o[4 * j + rr], 0, 0,
-                                                                               0, 127, 0, psc[rr]);
-              pin_agpr(o[4 * j + rr]);
-              if (with_a) part_a(4 * j + rr, key0, need_mask);
-              __builtin_amdgcn_sched_barrier(0);
-            }
+          for (int k = 0; k < 16; ++k) {
+            const int idx = kOrder[k], j = idx >> 2, rr = idx & 3;
+            fence_v(vb[j & 1]);
+            o[idx] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb[j & 1], pt[rr], o[idx], 0, 0, 0, 127, 0,
+                                                                     psc[rr]);
+            pin_agpr(o[idx]);
+            if (with_a) part_a(k, key0, need_mask);
+            if (k == 4) vb[0] = vread(st, 4 * wave + 2);
+            if (k == 7) vb[1] = vread(st, 4 * wave + 3);
+            __builtin_amdgcn_sched_barrier(0);
           }
         };
 
