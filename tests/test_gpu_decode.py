@@ -422,3 +422,36 @@ def test_fp16_large_score_growth_is_recomputed():
     x.kv_cache[:] = kv.astype(np.float16).view(np.uint16)
     out, lse = run_gpu(x)
     assert_parity(x, out, lse, run_oracle(x))
+
+
+# ---------------------------------------------------------------- large batches, long pages, short plans
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+@pytest.mark.parametrize("splits", [0, 37])
+def test_large_batch_with_empty_and_short_sequences(dtype, splits):
+    """300 sequences (several per lane of the workgroups' prefix sum), zeros and lengths below q_len
+    included; the planned split and a forced odd one."""
+    rng = np.random.default_rng(401)
+    lens = rng.integers(0, 600, size=300)
+    lens[::17] = 0
+    lens[5::23] = 1
+    x = mi.make_inputs(300, 2, 16, dtype, ("list", lens.tolist()), seed=402)
+    print(f"B=300 splits={splits} dtype={dtype} keys={int(lens.sum())}", flush=True)
+    out, lse = run_gpu(x, opts=mla.options(num_splits=splits) if splits else None)
+    assert_parity(x, out, lse, run_oracle(x))
+
+
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+def test_pages_of_many_tiles(dtype):
+    x = mi.make_inputs(2, 4, 32, dtype, ("list", [3000, 1100]), page_size=1024, seed=403)
+    out, lse = run_gpu(x)
+    assert_parity(x, out, lse, run_oracle(x))
+
+
+def test_lengths_above_the_planned_maximum():
+    """A sequence longer than the max_seq_len the plan was made for is still decoded correctly
+    (only the balance of the split suffers)."""
+    x = mi.make_inputs(3, 4, 32, mi.FP8_E4M3, ("list", [1000, 50, 2500]), seed=404)
+    q, kv, bt, sl = to_dev(x)
+    out, lse = mla.decode(q, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_seq_len=100)
+    torch.cuda.synchronize()
+    assert_parity(x, out, lse, run_oracle(x))
