@@ -26,11 +26,14 @@ namespace {
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint8_t lds_t;
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __attribute__((address_space(3))) v4i lds_v4i;
@@ -254,14 +257,13 @@ __device__ __forceinline__ long long readlane_ll(long long v, int l) {
 }
 
 // two probabilities in the PV operand format (bf16 or fp16, round to nearest even)
+// (one v_cvt_pk_{bf16,f16}_f32; a lands in the low half)
 template <int DT>
 __device__ __forceinline__ uint32_t pack_p16x2(float a, float b) {
   if constexpr (DT == kFp16) {
-    const _Float16 x = (_Float16)a, y = (_Float16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2h));
   } else {
-    const __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
   }
 }
 template <int DT>
@@ -275,8 +277,7 @@ __device__ __forceinline__ v16f pv_mfma_h16(const v4i& v, const v4i& pw, const v
   }
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
 }
 
 // Epilogue stores: the final O of a sequence held by one slice goes out
@@ -914,17 +915,20 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           const v2i r0i = __builtin_bit_cast(v2i, r0), r1i = __builtin_bit_cast(v2i, r1);
           return v4i{r0i[0], r0i[1], r1i[0], r1i[1]};
         };
+        // LDS operands are read several MFMAs ahead (K four, V two blocks): one
+        // 16-bit MFMA (32 cycles) is shorter than the latency of an LDS read
+        constexpr int kAhead = 4, kVAhead = 2;
         auto qk = [&](const lds_t* st, v16f& s) {
           s = v16f{0};
-          v4i a = kread(st, 0);
+          v4i a[kAhead];
+#pragma unroll
+          for (int c = 0; c < kAhead; ++c) a[c] = kread(st, c);
 #pragma unroll
           for (int c = 0; c < 36; ++c) {
-            v4i an = a;
-            if (c + 1 < 36) an = kread(st, c + 1);
             const v4i qb = v4i{qreg[c][0], qreg[c][1], qreg[c][2], qreg[c][3]};
-            qk_mfma_h16<DT>(s, a, qb, c == 35);
+            qk_mfma_h16<DT>(s, a[c % kAhead], qb, c == 35);
+            if (c + kAhead < 36) a[c % kAhead] = kread(st, c + kAhead);
             __builtin_amdgcn_sched_barrier(0);
-            a = an;
           }
         };
         float mx_raw = -INFINITY, mref = 0.f, lsum = 0.f;
@@ -971,20 +975,23 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           }
         };
         auto pv = [&](const lds_t* st, const v4i& p0, const v4i& p1, bool with_sm, int key0, bool need_mask) {
-          v4i vt0 = vread(st, 0, 0), vt1 = vread(st, 0, 1);
+          v4i vt[kVAhead][2];
+#pragma unroll
+          for (int db = 0; db < kVAhead; ++db) {
+            vt[db][0] = vread(st, db, 0);
+            vt[db][1] = vread(st, db, 1);
+          }
 #pragma unroll
           for (int db = 0; db < 16; ++db) {
-            v4i vn0 = vt0, vn1 = vt1;
-            if (db + 1 < 16) {
-              vn0 = vread(st, db + 1, 0);
-              vn1 = vread(st, db + 1, 1);
+            const int sl = db % kVAhead;
+            o[db] = pv_mfma_h16<DT>(vt[sl][0], p0, o[db]);
+            o[db] = pv_mfma_h16<DT>(vt[sl][1], p1, o[db]);
+            if (db + kVAhead < 16) {
+              vt[sl][0] = vread(st, db + kVAhead, 0);
+              vt[sl][1] = vread(st, db + kVAhead, 1);
             }
-            o[db] = pv_mfma_h16<DT>(vt0, p0, o[db]);
-            o[db] = pv_mfma_h16<DT>(vt1, p1, o[db]);
             if (with_sm && db < 8) sm_chunk(db, key0, need_mask);
             __builtin_amdgcn_sched_barrier(0);
-            vt0 = vn0;
-            vt1 = vn1;
           }
         };
 
