@@ -14,9 +14,10 @@ order of draws:
   4. the page pool ~ N(0, 1), shape [num_pages, page_size, 576], drawn in
      chunks of 256 pages in page order (for FP8 the stream is replayed: a
      first pass finds the pool's amax, a second quantises).
-bf16 inputs are cast round-to-nearest-even; FP8 inputs use one per-tensor
+bf16 inputs are cast round-to-nearest-even (fp16 likewise); FP8 inputs use one per-tensor
 scale amax/448 each for q and for the cache, clamp to +-448 and cast to OCP
-E4M3 (e4m3fn), so dequantised value = code * scale.  Spare pages are filled
+E4M3 (e4m3fn), so dequantised value = code * scale.  The mixed code takes bf16
+q and an E4M3 cache (the same draws).  Spare pages are filled
 with NaN codes; block_table entries past a sequence's last page point at a
 spare page; rows past seq_len inside a sequence's last page keep their N(0,1)
 draws (optionally NaN with ``poison_tail``).
@@ -33,6 +34,7 @@ D_V = 512
 BF16 = 1
 FP8_E4M3 = 2
 FP16 = 3
+BF16_Q_E4M3_KV = 4  # bf16 q over an OCP E4M3 cache
 NAN_BF16 = 0x7FC0
 NAN_F16 = 0x7E00
 NAN_E4M3 = 0x7F
@@ -44,17 +46,21 @@ WORKLOADS = {
     "agentic_b16_q4_h32_fp8_80k": dict(index=3, B=16, q_len=4, H=32, dtype=FP8_E4M3, lens=("fixed", 81920), spare_pages=64),
     "dsv3_b64_q1_h128_bf16_ragged": dict(index=4, B=64, q_len=1, H=128, dtype=BF16, lens=("uniform", 4096, 65536), spare_pages=64),
     "spec_b128_q4_h64_fp8_ragged": dict(index=5, B=128, q_len=4, H=64, dtype=FP8_E4M3, lens=("loguniform", 1024, 81920), spare_pages=64),
+    # bf16 queries over the FP8 cache of the batch-4 agentic shape (mixed inputs; not one of the five
+    # configurations above)
+    "agentic_b4_q4_h32_bf16q_fp8kv_80k": dict(index=6, B=4, q_len=4, H=32, dtype=BF16_Q_E4M3_KV,
+                                              lens=("fixed", 81920), spare_pages=64),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
 
 @dataclass
 class DecodeInputs:
-    q: np.ndarray              # uint16 bf16 bits or uint8 e4m3 codes, [B, q_len, H, 576]
-    kv_cache: np.ndarray       # same dtype, [num_pages, page_size, 576]
+    q: np.ndarray              # uint16 bf16 / fp16 bits or uint8 e4m3 codes, [B, q_len, H, 576]
+    kv_cache: np.ndarray       # same format (e4m3 for the mixed code), [num_pages, page_size, 576]
     block_table: np.ndarray    # int32 [B, max_pages]
     seq_lens: np.ndarray       # int32 [B]
-    dtype: int                 # BF16 or FP8_E4M3
+    dtype: int                 # BF16, FP16, FP8_E4M3 or BF16_Q_E4M3_KV
     q_scale: float
     kv_scale: float
     softmax_scale: float
@@ -100,6 +106,16 @@ def _cast_e4m3(x: np.ndarray, scale: float) -> np.ndarray:
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)) / np.float32(scale)
     t = t.clamp_(-448.0, 448.0)
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def q_format(dtype: int) -> int:
+    """Storage format of q for a dtype code (bf16 for the mixed code)."""
+    return BF16 if dtype == BF16_Q_E4M3_KV else dtype
+
+
+def kv_format(dtype: int) -> int:
+    """Storage format of the cache rows for a dtype code (E4M3 for the mixed code)."""
+    return FP8_E4M3 if dtype == BF16_Q_E4M3_KV else dtype
 
 
 def _quantize(x: np.ndarray, dtype: int):
@@ -186,10 +202,10 @@ def make_inputs(B, q_len, H, dtype, lens, *, page_size=64, seed=0, spare_pages=8
     if pool_pages is not None and B == 1:
         block_table[0, :] = perm[:max_pages]
     q32 = rng.standard_normal((B, q_len, H, D_QK), dtype=np.float32)
-    q, q_scale = _quantize(q32, dtype)
+    q, q_scale = _quantize(q32, q_format(dtype))
     del q32
-    kv, kv_scale = _draw_pool(rng, num_pages, page_size, dtype)
-    nan_code = {BF16: NAN_BF16, FP16: NAN_F16}.get(dtype, NAN_E4M3)
+    kv, kv_scale = _draw_pool(rng, num_pages, page_size, kv_format(dtype))
+    nan_code = {BF16: NAN_BF16, FP16: NAN_F16}.get(kv_format(dtype), NAN_E4M3)
     used = np.zeros(num_pages, dtype=bool)
     for b in range(B):
         used[block_table[b, :int(pages_per_seq[b])]] = True

@@ -33,6 +33,7 @@ _lib = None
 BF16 = 1
 FP8_E4M3 = 2
 FP16 = 3
+BF16_Q_E4M3_KV = 4  # bf16 q over an e4m3 cache
 D_QK = 576
 D_V = 512
 
@@ -119,8 +120,9 @@ def mla_decode(q, kv_cache, block_table, seq_lens, *, dtype: int, softmax_scale:
                num_threads: int = 0, want_absv: bool = False):
     """fp64 MLA decode.
 
-    q: uint16 (bf16 or fp16 bits) or uint8 (e4m3 codes) array [B, q_len, H, 576]; dtype BF16, FP16 or FP8_E4M3.
-    kv_cache: same dtype, [num_pages, page_size, 576].
+    q: uint16 (bf16 or fp16 bits) or uint8 (e4m3 codes) array [B, q_len, H, 576]; dtype BF16, FP16, FP8_E4M3
+    or BF16_Q_E4M3_KV (bf16 q bits, e4m3 cache codes).
+    kv_cache: same format as q (e4m3 for BF16_Q_E4M3_KV), [num_pages, page_size, 576].
     block_table: int32 [B, max_pages]; seq_lens: int32 [B].
     Returns (O float64 [B, q_len, H, 512], LSE float64 [B, q_len, H]).
     split_len > 0 computes per-chunk partials and merges them by LSE.
@@ -133,8 +135,9 @@ def mla_decode(q, kv_cache, block_table, seq_lens, *, dtype: int, softmax_scale:
     kv_cache = np.ascontiguousarray(kv_cache)
     block_table = np.ascontiguousarray(block_table, dtype=np.int32)
     seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
-    want = np.uint8 if dtype == FP8_E4M3 else np.uint16
-    if q.dtype != want or kv_cache.dtype != want:
+    want_q = np.uint8 if dtype == FP8_E4M3 else np.uint16
+    want_kv = np.uint8 if dtype in (FP8_E4M3, BF16_Q_E4M3_KV) else np.uint16
+    if q.dtype != want_q or kv_cache.dtype != want_kv:
         raise TypeError("q and kv_cache must hold raw bf16 / fp16 bits (uint16) or e4m3 codes (uint8)")
     B, q_len, H, dq = q.shape
     num_pages, page_size, dk = kv_cache.shape

@@ -30,6 +30,9 @@
  *     `split_len` keys; each chunk yields a normalised partial O_s and
  *     lse_s; they are merged as LSE = ln sum_s exp(lse_s) and
  *     O = sum_s exp(lse_s - LSE) * O_s.  This must equal the unsplit result.
+ *   - Mixed inputs (tokenspeed-mla package page, "What it is": FP16, BF16
+ *     and FP8 decode; the reading taken here is bf16 queries over an FP8
+ *     E4M3 cache): q is decoded as bf16 and every cache row as E4M3.
  *   - Decoders are written from the format definitions: bf16 is the top 16
  *     bits of an IEEE binary32; OCP FP8 E4M3 has bias 7, no infinities,
  *     S.1111.111 = NaN, subnormals m/8 * 2^-6.
@@ -48,7 +51,10 @@
 #define ORC_D_QK 576
 #define ORC_D_V 512
 
-enum { ORC_BF16 = 1, ORC_FP8_E4M3 = 2, ORC_FP16 = 3 };
+enum { ORC_BF16 = 1, ORC_FP8_E4M3 = 2, ORC_FP16 = 3, ORC_BF16_Q_E4M3_KV = 4 };
+/* element formats of q and of the cache rows for a dtype code */
+static int q_format(int dtype) { return dtype == ORC_BF16_Q_E4M3_KV ? ORC_BF16 : dtype; }
+static int kv_format(int dtype) { return dtype == ORC_BF16_Q_E4M3_KV ? ORC_FP8_E4M3 : dtype; }
 
 double oracle_dec_bf16(uint16_t bits) {
   uint32_t u = (uint32_t)bits << 16;
@@ -153,8 +159,9 @@ static int attend_range(const void* kv, int dtype, const int32_t* bt_row, int nu
 }
 
 /*
- * q:          [B, q_len, H, 576] bf16 bits or e4m3 codes
- * kv:         [num_pages, page_size, 576], same dtype as q
+ * q:          [B, q_len, H, 576] bf16 / fp16 bits or e4m3 codes
+ * kv:         [num_pages, page_size, 576], same format as q, except for
+ *             ORC_BF16_Q_E4M3_KV: bf16 q, e4m3 cache
  * block_table:[B, max_pages] int32 (row stride max_pages)
  * seq_lens:   [B] int32
  * out:        [B, q_len, H, 512] fp64;  lse: [B, q_len, H] fp64
@@ -169,7 +176,8 @@ int oracle_mla_decode(const void* q, const void* kv, int dtype, const int32_t* b
                       double softmax_scale, double q_scale, double kv_scale, int split_len, int window,
                       double* out, double* lse, double* absv, int num_threads) {
   if (!q || !kv || !block_table || !seq_lens || !out || !lse) return -2;
-  if (dtype != ORC_BF16 && dtype != ORC_FP8_E4M3 && dtype != ORC_FP16) return -2;
+  if (dtype != ORC_BF16 && dtype != ORC_FP8_E4M3 && dtype != ORC_FP16 && dtype != ORC_BF16_Q_E4M3_KV) return -2;
+  const int qfmt = q_format(dtype), kvfmt = kv_format(dtype);
   if (B < 0 || q_len <= 0 || H <= 0 || page_size <= 0 || max_pages < 0 || split_len < 0 || window < 0) return -2;
   if (absv && split_len > 0) return -2;
   for (int b = 0; b < B; ++b) {
@@ -198,10 +206,10 @@ int oracle_mla_decode(const void* q, const void* kv, int dtype, const int32_t* b
     double* lse_s = (double*)malloc(sizeof(double) * (size_t)H);
     double* o_acc = out + row0 * ORC_D_V;
     double* lse_acc = lse + row0;
-    for (int h = 0; h < H; ++h) decode_row(q, dtype, (row0 + h) * ORC_D_QK, ORC_D_QK, q_scale, qv + (size_t)h * ORC_D_QK);
+    for (int h = 0; h < H; ++h) decode_row(q, qfmt, (row0 + h) * ORC_D_QK, ORC_D_QK, q_scale, qv + (size_t)h * ORC_D_QK);
     const int32_t* bt_row = block_table + (size_t)b * max_pages;
     if (split_len == 0) {
-      if (attend_range(kv, dtype, bt_row, num_pages, page_size, lo, n, H, qv, softmax_scale, kv_scale, scores, row,
+      if (attend_range(kv, kvfmt, bt_row, num_pages, page_size, lo, n, H, qv, softmax_scale, kv_scale, scores, row,
                        o_acc, lse_acc, absv ? absv + row0 * ORC_D_V : NULL) != 0)
         st = -1;
     } else {
@@ -212,7 +220,7 @@ int oracle_mla_decode(const void* q, const void* kv, int dtype, const int32_t* b
       double* all_l = (double*)malloc(sizeof(double) * (size_t)nsplit * H);
       for (int s = 0; s < nsplit && st == 0; ++s) {
         int j0 = lo + s * chunk, j1 = j0 + chunk < n ? j0 + chunk : n;
-        if (attend_range(kv, dtype, bt_row, num_pages, page_size, j0, j1, H, qv, softmax_scale, kv_scale, scores, row,
+        if (attend_range(kv, kvfmt, bt_row, num_pages, page_size, j0, j1, H, qv, softmax_scale, kv_scale, scores, row,
                          all_o + (size_t)s * H * ORC_D_V, all_l + (size_t)s * H, NULL) != 0)
           st = -1;
       }

@@ -1,7 +1,7 @@
 """Dense brute-force MLA decode for tiny shapes: an independent pin of the oracle.
 
 It shares nothing with ``oracle/``: stored values are decoded with torch's
-own bf16 / float8_e4m3fn conversions, the paged cache is first gathered into
+own bf16 / float16 / float8_e4m3fn conversions (q and the cache each in its own format), the paged cache is first gathered into
 a dense [L, 576] key matrix in logical order, the causal (and sliding-window)
 mask is an explicit boolean matrix, and the softmax / log-sum-exp come from scipy.
 """
@@ -28,8 +28,8 @@ def dense_keys(kv: np.ndarray, block_table: np.ndarray, b: int, L: int) -> np.nd
 
 
 def brute_decode(x: "mi.DecodeInputs", *, alignment: str = "bottom_right", window: int = 0):
-    q = decode_values(x.q, x.dtype) * x.q_scale
-    kv = decode_values(x.kv_cache, x.dtype) * x.kv_scale
+    q = decode_values(x.q, mi.q_format(x.dtype)) * x.q_scale
+    kv = decode_values(x.kv_cache, mi.kv_format(x.dtype)) * x.kv_scale
     B, q_len, H, _ = q.shape
     O = np.zeros((B, q_len, H, 512))
     lse = np.full((B, q_len, H), -np.inf)

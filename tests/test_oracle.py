@@ -107,6 +107,8 @@ SHAPES = [
     (3, 4, 2, mi.BF16, [0, 4, 300], 64),
     (2, 3, 5, mi.FP8_E4M3, [1, 130], 64),
     (1, 2, 8, mi.BF16, [257], 1),
+    (2, 4, 6, mi.BF16_Q_E4M3_KV, [3, 170], 16),  # bf16 q over an e4m3 cache
+    (1, 3, 4, mi.BF16_Q_E4M3_KV, [129], 64),
 ]
 
 
@@ -183,6 +185,7 @@ WINDOW_SHAPES = [
     (1, 2, 8, mi.BF16, [257], 16, 100),
     (2, 1, 3, mi.FP8_E4M3, [40, 77], 16, 1000),
     (2, 4, 3, mi.FP16, [90, 7], 16, 30),
+    (2, 4, 3, mi.BF16_Q_E4M3_KV, [60, 9], 16, 25),
 ]
 
 
