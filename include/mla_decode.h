@@ -67,7 +67,9 @@ typedef enum mla_status {
 typedef enum mla_dtype {
   MLA_DTYPE_BF16 = 1,     /* bfloat16, stored as 16-bit patterns */
   MLA_DTYPE_FP8_E4M3 = 2, /* OCP FP8 E4M3 (e4m3fn): bias 7, no inf, S.1111.111 = NaN, max 448 */
-  MLA_DTYPE_FP16 = 3      /* IEEE binary16 (tokenspeed-mla package page: FP16 / BF16 / FP8 decode inputs) */
+  MLA_DTYPE_FP16 = 3,     /* IEEE binary16 (tokenspeed-mla package page: FP16 / BF16 / FP8 decode inputs) */
+  MLA_DTYPE_BF16_Q_FP8_KV = 4 /* bf16 q over an OCP FP8 E4M3 kv_cache (the same package page's
+                                 FP8 decode, with queries kept in bf16) */
 } mla_dtype;
 
 /* Sizes of one decode call.  All fields are element counts. */
@@ -80,7 +82,7 @@ typedef struct mla_shape {
   int32_t max_pages;   /* entries per block_table row (its row stride), >= 1 */
   int32_t max_seq_len; /* the length the workspace was planned for (upper bound of seq_lens);
                           0 <= max_seq_len <= max_pages * page_size */
-  int32_t dtype;       /* mla_dtype of q and kv_cache (both the same) */
+  int32_t dtype;       /* mla_dtype of q and kv_cache (both the same, except MLA_DTYPE_BF16_Q_FP8_KV) */
 } mla_shape;
 
 /*
@@ -106,8 +108,10 @@ int mla_get_split_kv_and_workspace(int32_t batch, int32_t q_len, int32_t num_hea
  * MLA decode (the operation described at the top of this file).
  *
  *   shape       host pointer to the call's sizes.
- *   q           device, [batch, q_len, num_heads, 576] of shape->dtype, contiguous, 16-byte aligned.
- *   kv_cache    device, [num_pages, page_size, 576] of shape->dtype, contiguous, 16-byte aligned.
+ *   q           device, [batch, q_len, num_heads, 576] of shape->dtype (bf16 for
+ *               MLA_DTYPE_BF16_Q_FP8_KV), contiguous, 16-byte aligned.
+ *   kv_cache    device, [num_pages, page_size, 576] of shape->dtype (E4M3 for
+ *               MLA_DTYPE_BF16_Q_FP8_KV), contiguous, 16-byte aligned.
  *   block_table device int32, [batch, max_pages] row-major.  The first
  *               ceil(seq_lens[b] / page_size) entries of row b must be page
  *               indices in [0, num_pages); later entries are never read.
@@ -118,7 +122,11 @@ int mla_get_split_kv_and_workspace(int32_t batch, int32_t q_len, int32_t num_hea
  *               max_seq_len are still computed correctly (less balanced).
  *   softmax_scale, q_scale, kv_scale
  *               host floats; dequantised value = stored value * scale (pass
- *               1.0 for bf16 and fp16 data).
+ *               1.0 for bf16 and fp16 data).  The scores are formed exactly
+ *               from the stored values (bf16 x E4M3 products are exact in
+ *               the fp32 accumulation's inputs); P is rounded to bf16 for the
+ *               PV product except in the all-FP8 path, where it is E4M3 with a
+ *               per-row power-of-two scale.
  *   out         device bf16 [batch, q_len, num_heads, 512], contiguous, 16-byte aligned.
  *   lse         device fp32 [batch, q_len, num_heads] or NULL to skip.
  *   workspace   device scratch of workspace_bytes bytes, 256-byte aligned, at

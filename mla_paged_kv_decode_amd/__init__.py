@@ -23,6 +23,7 @@ D_V = 512
 DTYPE_BF16 = 1
 DTYPE_FP8_E4M3 = 2
 DTYPE_FP16 = 3
+DTYPE_BF16_Q_FP8_KV = 4  # bf16 q over an E4M3 cache
 
 STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_DTYPE", -3: "MLA_ERR_SHAPE", -4: "MLA_ERR_ALIGN",
           -5: "MLA_ERR_WORKSPACE", -6: "MLA_ERR_UNSUPPORTED", -7: "MLA_ERR_HIP", -8: "MLA_ERR_DEVICE"}
@@ -141,13 +142,23 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _pair_code(q, kv_cache) -> int:
+    """mla_dtype of a (q, kv_cache) pair: one format for both, or bf16 q over an E4M3 cache."""
+    qc, kc = _dtype_code(q), _dtype_code(kv_cache)
+    if qc == kc:
+        return qc
+    if qc == DTYPE_BF16 and kc == DTYPE_FP8_E4M3:
+        return DTYPE_BF16_Q_FP8_KV
+    raise TypeError("q and kv_cache must have the same dtype, or be bf16 q over an E4M3 cache")
+
+
 def make_shape(q, kv_cache, block_table, max_seq_len: int) -> MlaShape:
     s = MlaShape()
     s.batch, s.q_len, s.num_heads = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
     s.num_pages, s.page_size = int(kv_cache.shape[0]), int(kv_cache.shape[1])
     s.max_pages = int(block_table.shape[1])
     s.max_seq_len = int(max_seq_len)
-    s.dtype = _dtype_code(q)
+    s.dtype = _pair_code(q, kv_cache)
     return s
 
 
@@ -157,8 +168,7 @@ def _check_layout(q, kv_cache, block_table, seq_lens):
         raise ValueError("q must be a contiguous [B, q_len, H, 576] tensor")
     if kv_cache.dim() != 3 or kv_cache.shape[2] != D_QK or not kv_cache.is_contiguous():
         raise ValueError("kv_cache must be a contiguous [num_pages, page_size, 576] tensor")
-    if _dtype_code(q) != _dtype_code(kv_cache):
-        raise TypeError("q and kv_cache must have the same dtype")
+    _pair_code(q, kv_cache)
     if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
         raise ValueError("block_table must be int32 [B, max_pages] with unit column stride")
     if block_table.stride(0) != block_table.shape[1]:
@@ -173,7 +183,7 @@ def decode(q, kv_cache, block_table, seq_lens, softmax_scale: float, q_scale: fl
     """MLA decode through the C ABI.  Tensors live on the current HIP device.
 
     q: [B, q_len, H, 576] bfloat16, float16 or float8_e4m3fn; kv_cache: [num_pages,
-    page_size, 576] of the same dtype; block_table: int32 [B, max_pages];
+    page_size, 576] of the same dtype (or float8_e4m3fn under bfloat16 q); block_table: int32 [B, max_pages];
     seq_lens: int32 [B].  Returns (out bf16 [B, q_len, H, 512], lse fp32
     [B, q_len, H] or None).  max_seq_len defaults to max(seq_lens), which
     reads seq_lens back to the host (pass it to avoid that synchronisation).

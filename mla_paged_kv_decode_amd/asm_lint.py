@@ -23,7 +23,7 @@ from __future__ import annotations
 import re
 
 MFMA_RESULT_WAITS = 20   # 16-pass XDL result -> any read (vendor tables give ~19 on gfx950)
-VALU_TO_MFMA_WAITS = 3   # VALU VGPR write -> MFMA source read
+VALU_TO_MFMA_WAITS = 2   # non-dot VALU VGPR write -> MFMA source read (the compiler's own gfx950 figure)
 
 
 def _regs(tok: str) -> set:

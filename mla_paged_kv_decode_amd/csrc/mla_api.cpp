@@ -165,8 +165,11 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
   if (opt && (opt->stages < 0 || opt->stages > 2)) return fail(MLA_ERR_SHAPE, "options.stages must be 0, 1 or 2");
   if (opt && opt->window < 0) return fail(MLA_ERR_SHAPE, "options.window must be >= 0 (got %d)", opt->window);
   if (!s) return fail(MLA_ERR_NULL, "shape is NULL");
-  if (s->dtype != MLA_DTYPE_BF16 && s->dtype != MLA_DTYPE_FP8_E4M3 && s->dtype != MLA_DTYPE_FP16)
-    return fail(MLA_ERR_DTYPE, "dtype %d is not MLA_DTYPE_BF16, MLA_DTYPE_FP16 or MLA_DTYPE_FP8_E4M3", s->dtype);
+  if (s->dtype != MLA_DTYPE_BF16 && s->dtype != MLA_DTYPE_FP8_E4M3 && s->dtype != MLA_DTYPE_FP16 &&
+      s->dtype != MLA_DTYPE_BF16_Q_FP8_KV)
+    return fail(MLA_ERR_DTYPE,
+                "dtype %d is not MLA_DTYPE_BF16, MLA_DTYPE_FP16, MLA_DTYPE_FP8_E4M3 or MLA_DTYPE_BF16_Q_FP8_KV",
+                s->dtype);
   int rc = check_plan_args(s->batch, s->q_len, s->num_heads, s->max_seq_len);
   if (rc) return rc;
   if (s->num_pages < 1) return fail(MLA_ERR_SHAPE, "num_pages must be >= 1 (got %d)", s->num_pages);
@@ -202,7 +205,10 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
                   pl.bytes);
   }
 
-  const int dt = s->dtype == MLA_DTYPE_FP8_E4M3 ? mla::kFp8 : s->dtype == MLA_DTYPE_FP16 ? mla::kFp16 : mla::kBf16;
+  const int dt = s->dtype == MLA_DTYPE_FP8_E4M3      ? mla::kFp8
+                 : s->dtype == MLA_DTYPE_FP16         ? mla::kFp16
+                 : s->dtype == MLA_DTYPE_BF16_Q_FP8_KV ? mla::kMixed
+                                                      : mla::kBf16;
   int shift = 0;
   while ((1 << shift) < s->page_size) ++shift;
   mla::PartialParams p{};
@@ -234,7 +240,7 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
   p.v_scale = kv_scale;
   p.part_bf16 = pl.part_bf16;
   p.window = opt ? opt->window : 0;
-  const int tile = dt == mla::kFp8 ? 64 : 32;
+  const int tile = (dt == mla::kFp8 || dt == mla::kMixed) ? 64 : 32;  // keys per LDS tile
   hipStream_t st = (hipStream_t)stream;
   const int stages = opt ? opt->stages : 0;
   hipError_t e = hipSuccess;

@@ -16,7 +16,8 @@ constexpr int kStages = 4;      // LDS ring of KV tiles
 constexpr int kStageBytes = 36864;  // 64 fp8 rows or 32 bf16 rows of 576 elements
 constexpr int kThreads = 256;
 
-enum KernelDtype { kBf16 = 1, kFp8 = 2, kFp16 = 3 };
+// kMixed: bf16 q over an OCP E4M3 cache
+enum KernelDtype { kBf16 = 1, kFp8 = 2, kFp16 = 3, kMixed = 4 };
 
 // Everything the split-KV partial kernel needs.  Passed by value.
 struct PartialParams {

@@ -18,6 +18,8 @@
 //    page, fused K/V pack + FP8 quantisation).
 #include <math.h>
 
+#include <type_traits>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -84,6 +86,8 @@ struct Traits<kBf16> {
 };
 template <>
 struct Traits<kFp16> : Traits<kBf16> {};  // same 2-byte rows and tiles
+template <>
+struct Traits<kMixed> : Traits<kFp8> {};  // E4M3 cache rows and tiles
 
 // LDS layout of a tile: row r, 16-byte chunk c lives at chunk slot
 // r * kChunks + (c ^ swz(r)).  The XOR keeps every access pattern of the
@@ -91,7 +95,7 @@ struct Traits<kFp16> : Traits<kBf16> {};  // same 2-byte rows and tiles
 // free of bank conflicts on the 64-bank LDS.
 template <int DT>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (DT == kFp8) {
+  if constexpr (DT == kFp8 || DT == kMixed) {
     return (r >> 2) & 3;
   } else {
     return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
@@ -278,6 +282,16 @@ __device__ __forceinline__ v16f pv_mfma_h16(const v4i& v, const v4i& pw, const v
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
+}
+// eight E4M3 codes (in byte order) -> eight bf16 values, exactly (every E4M3
+// value is a bf16 value)
+__device__ __forceinline__ v4i widen_e4m3_bf16(const v2i& x) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, true);
+  return v4i{__builtin_bit_cast(int, a), __builtin_bit_cast(int, b), __builtin_bit_cast(int, c),
+             __builtin_bit_cast(int, d)};
 }
 
 // Epilogue stores: the final O of a sequence held by one slice goes out
@@ -547,6 +561,18 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
       kaddr[1] = n * RB + (((2 * hh + 1) ^ sw) * 16);
       kaddr[2] = kaddr[3] = 0;
       // transposing V reads: source-lane roles inside each 16-lane group
+      const int grp = lane >> 4, hs = grp >> 1, dsub = grp & 1, uu = lane & 15, rr = uu >> 1, c8 = uu & 1;
+      const int kbase = 8 * (rr >> 2) + 4 * hs + (rr & 3);
+      const int s8 = (2 * (rr >> 2) + hs) & 3;
+      vaddr[0] = kbase * RB + (((0 + dsub) ^ s8) * 16) + 8 * c8;
+      vaddr[1] = kbase * RB + (((2 + dsub) ^ s8) * 16) + 8 * c8;
+      vaddr[2] = vaddr[3] = 0;
+    } else if constexpr (DT == kMixed) {
+      // K: eight E4M3 codes of key row n, dims [16c + 8hh, +8) (chunk c, half hh);
+      // V: the transposing 8-bit reads of the fp8 path, one read per operand
+      const int sw = (n >> 2) & 3;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) kaddr[x] = n * RB + ((x ^ sw) * 16) + 8 * hh;
       const int grp = lane >> 4, hs = grp >> 1, dsub = grp & 1, uu = lane & 15, rr = uu >> 1, c8 = uu & 1;
       const int kbase = 8 * (rr >> 2) + 4 * hs + (rr & 3);
       const int s8 = (2 * (rr >> 2) + hs) & 3;
@@ -902,32 +928,59 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         // the dummy loads of the last two iterations must land before LDS is reused
         wait_vm_barrier<0>();
       } else {
-        // ---------------- bf16: 32-key tiles, one 32x32 score block ----------------
+        // ------- bf16 / fp16 (and bf16 q over E4M3 tiles): one 32x32 score block per 32 keys -------
+        // A 64-key E4M3 tile is processed as two 32-key halves; its K and V
+        // operands are widened to bf16 in registers after the LDS read.
+        constexpr int CT = 32;               // keys per score block
+        constexpr int HALVES = TILE / CT;    // score blocks per LDS tile
+        constexpr int CDT = DT == kMixed ? kBf16 : DT;  // MFMA operand type
         issue_tile(0);
         if (1 < ntiles) issue_tile(1);
-        auto kread = [&](const lds_t* st, int c) -> v4i { return *(const lds_v4i*)(st + kaddr[c & 3] + 128 * (c >> 2)); };
-        auto vread = [&](const lds_t* st, int db, int u) -> v4i {
-          const int x = db & 1;
-          const int base0 = vaddr[x] + 128 * (db >> 1) + 16 * RB * u;
-          const int base1 = vaddr[2 + x] + 128 * (db >> 1) + 16 * RB * u;
-          const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(st + base0));
-          const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(st + base1));
-          const v2i r0i = __builtin_bit_cast(v2i, r0), r1i = __builtin_bit_cast(v2i, r1);
-          return v4i{r0i[0], r0i[1], r1i[0], r1i[1]};
+        // raw operands: bf16 / fp16 are MFMA-ready (v4i), E4M3 is widened first (v2i)
+        using raw_t = std::conditional_t<DT == kMixed, v2i, v4i>;
+        auto kread = [&](const lds_t* st, int c) -> raw_t {
+          if constexpr (DT == kMixed) {
+            return *(const lds_v2i*)(st + kaddr[c & 3] + 64 * (c >> 2));
+          } else {
+            return *(const lds_v4i*)(st + kaddr[c & 3] + 128 * (c >> 2));
+          }
+        };
+        auto vread = [&](const lds_t* st, int db, int u) -> raw_t {
+          if constexpr (DT == kMixed) {
+            return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(st + vaddr[db & 1] + 64 * (db >> 1) + 16 * RB * u));
+          } else {
+            const int x = db & 1;
+            const int base0 = vaddr[x] + 128 * (db >> 1) + 16 * RB * u;
+            const int base1 = vaddr[2 + x] + 128 * (db >> 1) + 16 * RB * u;
+            const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(st + base0));
+            const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(st + base1));
+            const v2i r0i = __builtin_bit_cast(v2i, r0), r1i = __builtin_bit_cast(v2i, r1);
+            return v4i{r0i[0], r0i[1], r1i[0], r1i[1]};
+          }
+        };
+        auto ready = [&](const raw_t& x) -> v4i {
+          if constexpr (DT == kMixed) {
+            return widen_e4m3_bf16(x);
+          } else {
+            return x;
+          }
         };
         // LDS operands are read several MFMAs ahead (K four, V two blocks): one
-        // 16-bit MFMA (32 cycles) is shorter than the latency of an LDS read
+        // 16-bit MFMA (32 cycles) is shorter than the latency of an LDS read.
+        // Widened operands are produced one MFMA ahead, in the previous one's shadow.
         constexpr int kAhead = 4, kVAhead = 2;
         auto qk = [&](const lds_t* st, v16f& s) {
           s = v16f{0};
-          v4i a[kAhead];
+          raw_t a[kAhead];
 #pragma unroll
           for (int c = 0; c < kAhead; ++c) a[c] = kread(st, c);
+          v4i cur = ready(a[0]);
 #pragma unroll
           for (int c = 0; c < 36; ++c) {
             const v4i qb = v4i{qreg[c][0], qreg[c][1], qreg[c][2], qreg[c][3]};
-            qk_mfma_h16<DT>(s, a[c % kAhead], qb, c == 35);
+            qk_mfma_h16<CDT>(s, cur, qb, c == 35);
             if (c + kAhead < 36) a[c % kAhead] = kread(st, c + kAhead);
+            if (c + 1 < 36) cur = ready(a[(c + 1) % kAhead]);
             __builtin_amdgcn_sched_barrier(0);
           }
         };
@@ -967,58 +1020,71 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             }
           } else if (i == 6 || i == 7) {
             const int u = i - 6;
-            pb[u] = v4i{(int)pack_p16x2<DT>(pvv[8 * u + 0], pvv[8 * u + 1]),
-                        (int)pack_p16x2<DT>(pvv[8 * u + 2], pvv[8 * u + 3]),
-                        (int)pack_p16x2<DT>(pvv[8 * u + 4], pvv[8 * u + 5]),
-                        (int)pack_p16x2<DT>(pvv[8 * u + 6], pvv[8 * u + 7])};
+            pb[u] = v4i{(int)pack_p16x2<CDT>(pvv[8 * u + 0], pvv[8 * u + 1]),
+                        (int)pack_p16x2<CDT>(pvv[8 * u + 2], pvv[8 * u + 3]),
+                        (int)pack_p16x2<CDT>(pvv[8 * u + 4], pvv[8 * u + 5]),
+                        (int)pack_p16x2<CDT>(pvv[8 * u + 6], pvv[8 * u + 7])};
             if (u == 1) l_acc += lsum;
           }
         };
         auto pv = [&](const lds_t* st, const v4i& p0, const v4i& p1, bool with_sm, int key0, bool need_mask) {
-          v4i vt[kVAhead][2];
+          raw_t vt[kVAhead][2];
 #pragma unroll
           for (int db = 0; db < kVAhead; ++db) {
             vt[db][0] = vread(st, db, 0);
             vt[db][1] = vread(st, db, 1);
           }
+          v4i w0 = ready(vt[0][0]), w1 = ready(vt[0][1]);
 #pragma unroll
           for (int db = 0; db < 16; ++db) {
             const int sl = db % kVAhead;
-            o[db] = pv_mfma_h16<DT>(vt[sl][0], p0, o[db]);
-            o[db] = pv_mfma_h16<DT>(vt[sl][1], p1, o[db]);
+            o[db] = pv_mfma_h16<CDT>(w0, p0, o[db]);
+            o[db] = pv_mfma_h16<CDT>(w1, p1, o[db]);
+            if constexpr (DT == kMixed) __builtin_amdgcn_sched_barrier(0);
             if (db + kVAhead < 16) {
               vt[sl][0] = vread(st, db + kVAhead, 0);
               vt[sl][1] = vread(st, db + kVAhead, 1);
+            }
+            if (db + 1 < 16) {
+              w0 = ready(vt[(db + 1) % kVAhead][0]);
+              w1 = ready(vt[(db + 1) % kVAhead][1]);
             }
             if (with_sm && db < 8) sm_chunk(db, key0, need_mask);
             __builtin_amdgcn_sched_barrier(0);
           }
         };
+        // score block v covers keys [k0 + 32v, +32) of LDS tile v / HALVES
+        auto block_base = [&](int v) -> const lds_t* {
+          return smem + ((v / HALVES) % kStages) * kStageBytes + (v % HALVES) * CT * RB;
+        };
+        auto block_needs_mask = [&](int key0) { return key0 + CT > lim_min || key0 < lo_max; };
+        const int nblocks = (k1 - k0 + CT - 1) / CT;
 
         wait_tile_barrier(min(1, ntiles - 1));
         if (2 < ntiles) issue_tile(2);
         v4i pp0 = v4i{0, 0, 0, 0}, pp1 = v4i{0, 0, 0, 0};
         if (wave_active) {
           qk(smem, sc);
-          const bool nm = tile_needs_mask(k0);
+          const bool nm = block_needs_mask(k0);
 #pragma unroll
           for (int i = 0; i < 8; ++i) sm_chunk(i, k0, nm);
           pp0 = pb[0];
           pp1 = pb[1];
         }
-        for (int tt = 1; tt < ntiles; ++tt) {
-          wait_tile_barrier(min(1, ntiles - 1 - tt));
-          if (tt + 2 < ntiles) issue_tile(tt + 2);
+        for (int v = 1; v < nblocks; ++v) {
+          if (v % HALVES == 0) {
+            const int tt = v / HALVES;
+            wait_tile_barrier(min(1, ntiles - 1 - tt));
+            if (tt + 2 < ntiles) issue_tile(tt + 2);
+          }
           if (!wave_active) continue;
-          const lds_t* st = smem + (tt % kStages) * kStageBytes;
-          const lds_t* stp = smem + ((tt - 1) % kStages) * kStageBytes;
-          const int key0 = k0 + tt * TILE;
-          qk(st, sc);
-          pv(stp, pp0, pp1, true, key0, tile_needs_mask(key0));
+          const int key0 = k0 + v * CT;
+          qk(block_base(v), sc);
+          pv(block_base(v - 1), pp0, pp1, true, key0, block_needs_mask(key0));
           pp0 = pb[0];
           pp1 = pb[1];
         }
-        if (wave_active) pv(smem + ((ntiles - 1) % kStages) * kStageBytes, pp0, pp1, false, 0, false);
+        if (wave_active) pv(block_base(nblocks - 1), pp0, pp1, false, 0, false);
       }
       // did any row of the workgroup outgrow its reference?
       const bool wave_ovf = __builtin_amdgcn_ballot_w64(ovf) != 0;
@@ -1507,35 +1573,27 @@ __global__ void __launch_bounds__(256) mla_kv_pack_fp8(PackParams p) {
 
 }  // namespace
 
+template <int DT>
+void launch_partial_dt(const PartialParams& p, bool fast_pages, bool win, dim3 grid, dim3 block, hipStream_t stream) {
+  if (fast_pages) {
+    if (win) hipLaunchKernelGGL((mla_split_kv_partial<DT, true, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((mla_split_kv_partial<DT, true, false>), grid, block, 0, stream, p);
+  } else {
+    if (win) hipLaunchKernelGGL((mla_split_kv_partial<DT, false, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((mla_split_kv_partial<DT, false, false>), grid, block, 0, stream, p);
+  }
+}
+
 hipError_t launch_partial(const PartialParams& p, int dtype, bool fast_pages, hipStream_t stream) {
   const dim3 grid((unsigned)(p.G * p.U)), block(kThreads);
   // kernels without a sliding window are separate instantiations, so the
   // window's per-row state costs them no registers
   const bool win = p.window > 0;
-  if (dtype == kFp8) {
-    if (fast_pages) {
-      if (win) hipLaunchKernelGGL((mla_split_kv_partial<kFp8, true, true>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((mla_split_kv_partial<kFp8, true, false>), grid, block, 0, stream, p);
-    } else {
-      if (win) hipLaunchKernelGGL((mla_split_kv_partial<kFp8, false, true>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((mla_split_kv_partial<kFp8, false, false>), grid, block, 0, stream, p);
-    }
-  } else if (dtype == kFp16) {
-    if (fast_pages) {
-      if (win) hipLaunchKernelGGL((mla_split_kv_partial<kFp16, true, true>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((mla_split_kv_partial<kFp16, true, false>), grid, block, 0, stream, p);
-    } else {
-      if (win) hipLaunchKernelGGL((mla_split_kv_partial<kFp16, false, true>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((mla_split_kv_partial<kFp16, false, false>), grid, block, 0, stream, p);
-    }
-  } else {
-    if (fast_pages) {
-      if (win) hipLaunchKernelGGL((mla_split_kv_partial<kBf16, true, true>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((mla_split_kv_partial<kBf16, true, false>), grid, block, 0, stream, p);
-    } else {
-      if (win) hipLaunchKernelGGL((mla_split_kv_partial<kBf16, false, true>), grid, block, 0, stream, p);
-      else hipLaunchKernelGGL((mla_split_kv_partial<kBf16, false, false>), grid, block, 0, stream, p);
-    }
+  switch (dtype) {
+    case kFp8: launch_partial_dt<kFp8>(p, fast_pages, win, grid, block, stream); break;
+    case kFp16: launch_partial_dt<kFp16>(p, fast_pages, win, grid, block, stream); break;
+    case kMixed: launch_partial_dt<kMixed>(p, fast_pages, win, grid, block, stream); break;
+    default: launch_partial_dt<kBf16>(p, fast_pages, win, grid, block, stream); break;
   }
   return hipGetLastError();
 }

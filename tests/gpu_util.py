@@ -19,21 +19,26 @@ LSE_TOL = 1e-3
 # u_P * sum_j w_j |V_j|.  The
 # result is rounded to bf16 (u = 2^-8 of the pre-rounding value).  A small absolute
 # slack covers fp32 accumulation order, exp2 and flushed fp8 subnormals.
-P_ROUND = {mi.BF16: 2.0 ** -8, mi.FP8_E4M3: 2.0 ** -4, mi.FP16: 2.0 ** -11}
+P_ROUND = {mi.BF16: 2.0 ** -8, mi.FP8_E4M3: 2.0 ** -4, mi.FP16: 2.0 ** -11, mi.BF16_Q_E4M3_KV: 2.0 ** -8}
 U_OUT = 2.0 ** -8
 SLACK = 2e-4
 
 
 def o_tol(dtype):
-    return FP8_O_TOL if dtype == mi.FP8_E4M3 else BF16_O_TOL
+    # an E4M3 cache (with either q) takes the FP8 bar
+    return FP8_O_TOL if mi.kv_format(dtype) == mi.FP8_E4M3 else BF16_O_TOL
+
+
+def _torch_dtype(fmt):
+    return {mi.BF16: torch.bfloat16, mi.FP16: torch.float16}.get(fmt, torch.float8_e4m3fn)
 
 
 def to_dev(x: "mi.DecodeInputs", dev="cuda:0"):
-    tdt = {mi.BF16: torch.bfloat16, mi.FP16: torch.float16}.get(x.dtype, torch.float8_e4m3fn)
-    raw_q = x.q if x.dtype == mi.FP8_E4M3 else x.q.view(np.int16)
-    raw_kv = x.kv_cache if x.dtype == mi.FP8_E4M3 else x.kv_cache.view(np.int16)
-    q = torch.from_numpy(np.ascontiguousarray(raw_q)).to(dev).view(tdt)
-    kv = torch.from_numpy(np.ascontiguousarray(raw_kv)).to(dev).view(tdt)
+    qf, kvf = mi.q_format(x.dtype), mi.kv_format(x.dtype)
+    raw_q = x.q if qf == mi.FP8_E4M3 else x.q.view(np.int16)
+    raw_kv = x.kv_cache if kvf == mi.FP8_E4M3 else x.kv_cache.view(np.int16)
+    q = torch.from_numpy(np.ascontiguousarray(raw_q)).to(dev).view(_torch_dtype(qf))
+    kv = torch.from_numpy(np.ascontiguousarray(raw_kv)).to(dev).view(_torch_dtype(kvf))
     bt = torch.from_numpy(np.ascontiguousarray(x.block_table)).to(dev)
     sl = torch.from_numpy(np.ascontiguousarray(x.seq_lens)).to(dev)
     return q, kv, bt, sl

@@ -104,6 +104,8 @@ def test_validation_errors_without_device():
     assert _decode_raw(None) == -1
     assert _decode_raw(_shape(dtype=7)) == -2
     assert _decode_raw(_shape(dtype=mla.DTYPE_FP16), kv=24) == -4  # fp16 is accepted, then validated
+    assert _decode_raw(_shape(dtype=mla.DTYPE_BF16_Q_FP8_KV), kv=24) == -4  # bf16 q / e4m3 cache likewise
+    assert _decode_raw(_shape(dtype=5)) == -2
     assert _decode_raw(_shape(page_size=48)) == -3
     assert _decode_raw(_shape(page_size=8)) == -3
     assert _decode_raw(_shape(q_len=0)) == -3
@@ -189,3 +191,17 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(mla, "LIB_PATH", "/nonexistent/libmla_decode.so")
     with pytest.raises(RuntimeError):
         mla.lib()
+
+
+def test_dtype_pairs_of_the_binding():
+    import torch
+
+    bf = torch.empty(1, 1, 1, 576, dtype=torch.bfloat16)
+    f8 = torch.empty(1, 64, 576, dtype=torch.float8_e4m3fn)
+    h = torch.empty(1, 64, 576, dtype=torch.float16)
+    assert mla._pair_code(bf, f8) == mla.DTYPE_BF16_Q_FP8_KV
+    assert mla._pair_code(bf, bf.view(1, 1, 576).expand(1, 64, 576)) == mla.DTYPE_BF16
+    with pytest.raises(TypeError):
+        mla._pair_code(f8.view(64, 1, 1, 576), bf)  # fp8 q over a bf16 cache is not a supported pair
+    with pytest.raises(TypeError):
+        mla._pair_code(bf, h)

@@ -43,7 +43,7 @@ def test_parity_small(B, q_len, H, dtype, lens, ps):
     assert_parity(x, out, lse, run_oracle(x))
 
 
-@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3, mi.BF16_Q_E4M3_KV])
 @pytest.mark.parametrize("splits", [1, 2, 3, 8, 64, 200])
 def test_forced_splits(dtype, splits):
     x = mi.make_inputs(3, 4, 32, dtype, ("list", [2500, 90, 1300]), seed=31)
@@ -52,7 +52,7 @@ def test_forced_splits(dtype, splits):
     assert_parity(x, out, lse, run_oracle(x))
 
 
-@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3, mi.BF16_Q_E4M3_KV])
 def test_fold_and_partial_precision_options(dtype):
     x = mi.make_inputs(2, 4, 16, dtype, ("list", [1800, 650]), seed=41)
     ref = run_oracle(x)
@@ -66,16 +66,17 @@ def test_fold_and_partial_precision_options(dtype):
     assert torch.equal(base, nofold) and torch.equal(lse_b, lse_n)
 
 
-@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3, mi.BF16_Q_E4M3_KV])
 def test_needles_are_bit_exact(dtype):
     """One-hot queries pick exactly one visible key; a masked needle just past the limit is ignored."""
     B, q_len, H, ps = 2, 4, 8, 64
     lens = [300, 1025]
     x = mi.make_inputs(B, q_len, H, dtype, ("list", lens), page_size=ps, seed=51)
     x.softmax_scale, x.q_scale, x.kv_scale = 1.0, 1.0, 1.0
-    one = np.uint16(0x3F80) if dtype == mi.BF16 else np.uint8(0x38)     # 1.0
-    big = np.uint16(0x4400) if dtype == mi.BF16 else np.uint8(0x7E)     # 512.0 / 448.0
-    bigger = np.uint16(0x4480) if dtype == mi.BF16 else np.uint8(0x7E)  # masked needle at least as large
+    q16, kv16 = mi.q_format(dtype) == mi.BF16, mi.kv_format(dtype) == mi.BF16
+    one = np.uint16(0x3F80) if q16 else np.uint8(0x38)      # 1.0
+    big = np.uint16(0x4400) if kv16 else np.uint8(0x7E)     # 512.0 / 448.0
+    bigger = np.uint16(0x4480) if kv16 else np.uint8(0x7E)  # masked needle at least as large
     x.q[:] = 0
     expected = {}
     dims = [(t * H + h) % 576 for t in range(q_len) for h in range(H)]
@@ -103,14 +104,14 @@ def test_needles_are_bit_exact(dtype):
                 expected[(b, t, h)] = j_star
     out, lse = run_gpu(x)
     O = out.cpu()
-    kv_t = torch.from_numpy(x.kv_cache.view(np.int16) if dtype == mi.BF16 else x.kv_cache)
-    kv_t = kv_t.view(torch.bfloat16 if dtype == mi.BF16 else torch.float8_e4m3fn)
+    kv_t = torch.from_numpy(x.kv_cache.view(np.int16) if kv16 else x.kv_cache)
+    kv_t = kv_t.view(torch.bfloat16 if kv16 else torch.float8_e4m3fn)
     for (b, t, h), j in expected.items():
         v = kv_t[x.block_table[b, j // ps], j % ps, :512].float().to(torch.bfloat16)
         assert torch.equal(O[b, t, h], v), (b, t, h, j)
 
 
-@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3, mi.BF16_Q_E4M3_KV])
 def test_page_relabelling_bit_identical(dtype):
     x = mi.make_inputs(3, 2, 32, dtype, ("list", [3000, 129, 2048]), seed=61)
     out, lse = run_gpu(x)
@@ -125,7 +126,7 @@ def test_page_relabelling_bit_identical(dtype):
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
-@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3, mi.BF16_Q_E4M3_KV])
 def test_nan_poisoned_tails_and_spares_are_never_read(dtype):
     x = mi.make_inputs(3, 4, 16, dtype, ("list", [70, 1, 1000]), page_size=64, seed=71, poison_tail=True)
     out, lse = run_gpu(x)
@@ -355,7 +356,7 @@ def test_window_parity(B, q_len, H, dtype, lens, ps, window):
     assert_parity(x, out, lse, run_oracle(x, window=window))
 
 
-@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3, mi.BF16_Q_E4M3_KV])
 @pytest.mark.parametrize("splits", [1, 3, 64])
 def test_window_forced_splits(dtype, splits):
     x = mi.make_inputs(3, 4, 32, dtype, ("list", [2500, 90, 1300]), seed=211)
@@ -424,6 +425,57 @@ def test_fp16_large_score_growth_is_recomputed():
     assert_parity(x, out, lse, run_oracle(x))
 
 
+# ---------------------------------------------------------------- bf16 q over an E4M3 cache
+MIXED_CASES = [
+    # B, q_len, H, lens, page_size, options
+    (3, 4, 32, [0, 77, 1000], 64, {}),
+    (2, 1, 128, [4096, 300], 64, {}),
+    (2, 4, 64, [1500, 3], 64, {"num_splits": 3}),
+    (4, 2, 16, [1, 2, 3, 130], 16, {}),  # pages shorter than a tile
+    (1, 3, 40, [901], 32, {}),
+    (3, 4, 32, [2500, 90, 1300], 64, {"num_splits": 64}),
+    (2, 4, 32, [2500, 700], 64, {"window": 37}),
+    (2, 2, 8, [333, 2], 256, {"partial_fp32": True, "num_splits": 5}),
+    (1, 5, 24, [97], 64, {}),  # an odd number of 32-key halves
+]
+
+
+@pytest.mark.parametrize("B,q_len,H,lens,ps,kw", MIXED_CASES)
+def test_bf16_q_fp8_cache_parity(B, q_len, H, lens, ps, kw):
+    x = mi.make_inputs(B, q_len, H, mi.BF16_Q_E4M3_KV, ("list", lens), page_size=ps, seed=500 + B * 5 + H + ps)
+    print(f"bf16 q / e4m3 cache B={B} q_len={q_len} H={H} lens={lens} ps={ps} {kw}", flush=True)
+    out, lse = run_gpu(x, opts=mla.options(**kw) if kw else None)
+    assert_parity(x, out, lse, run_oracle(x, window=kw.get("window", 0)),
+                  partial_fp32=bool(kw.get("partial_fp32", False)))
+
+
+def test_bf16_q_fp8_cache_every_code_widens_exactly():
+    """Every finite E4M3 code, subnormals included, sits in each key row; each row of the
+    query sees one key, so O must be that row's values exactly and LSE the one score,
+    which a one-hot query makes the code's value (every cache dimension is covered)."""
+    B, H = 5, 128
+    x = mi.make_inputs(B, 1, H, mi.BF16_Q_E4M3_KV, ("list", [1] * B), page_size=64, seed=521)
+    x.softmax_scale, x.q_scale, x.kv_scale = 1.0, 1.0, 1.0
+    codes = (np.arange(576) % 256).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0  # the two NaN codes
+    x.kv_cache[:] = codes
+    x.q[:] = 0
+    dims = {}
+    for b in range(B):
+        for h in range(H):
+            d = (b * H + h) % 576
+            x.q[b, 0, h, d] = 0x3F80  # bf16 1.0
+            dims[(b, h)] = d
+    out, lse = run_gpu(x)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn)
+    v_expect = vals[:512].to(torch.bfloat16)
+    O = out.cpu()
+    L = lse.cpu().numpy().astype(np.float64)
+    for (b, h), d in dims.items():
+        assert torch.equal(O[b, 0, h], v_expect), (b, h)
+        assert abs(L[b, 0, h] - float(vals[d].float())) <= 1e-6 * max(1.0, abs(float(vals[d].float()))), (b, h, d)
+
+
 # ---------------------------------------------------------------- large batches, long pages, short plans
 @pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
 @pytest.mark.parametrize("splits", [0, 37])
@@ -440,7 +492,7 @@ def test_large_batch_with_empty_and_short_sequences(dtype, splits):
     assert_parity(x, out, lse, run_oracle(x))
 
 
-@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3, mi.BF16_Q_E4M3_KV])
 def test_pages_of_many_tiles(dtype):
     x = mi.make_inputs(2, 4, 32, dtype, ("list", [3000, 1100]), page_size=1024, seed=403)
     out, lse = run_gpu(x)
