@@ -28,7 +28,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MLA decode µs/step + effective KV-read TB/s (q_len=4, 80K-token cache)"
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {1: 2500.0, 2: 5000.0}  # dense bf16 / fp8
+# dense MFMA peak of the path's contraction type: bf16, fp8, fp16, and bf16 for bf16 q over an
+# E4M3 cache (its operands are widened to bf16)
+MFMA_PEAK_TFLOPS = {1: 2500.0, 2: 5000.0, 3: 2500.0, 4: 2500.0}
+DTYPE_NAMES = {1: "bf16", 2: "fp8_e4m3", 3: "fp16", 4: "bf16_q.fp8_e4m3_kv"}
 MALL_BYTES = 256 << 20
 # published per-step latency for exactly this workload on the pages (another machine: context only)
 PAGES_US = {"agentic_b4_q4_h32_fp8_80k": 49.5, "agentic_b16_q4_h32_fp8_80k": 148.1}
@@ -44,11 +47,14 @@ def algorithmic(x) -> dict:
     """Algorithmic bytes / flops of one step (each KV row read once, no partials)."""
     import numpy as np
 
-    e = 1 if x.dtype == 2 else 2
+    import mla_inputs as mi
+
+    e = 1 if mi.kv_format(x.dtype) == mi.FP8_E4M3 else 2
+    eq = 1 if mi.q_format(x.dtype) == mi.FP8_E4M3 else 2
     L = x.seq_lens.astype(np.int64)
     B, q_len, H = x.B, x.q_len, x.H
     kv = int(L.sum()) * 576 * e
-    q = B * q_len * H * 576 * e
+    q = B * q_len * H * 576 * eq
     o = B * q_len * H * 512 * 2
     lse = B * q_len * H * 4
     bt = int(((L + x.page_size - 1) // x.page_size).sum()) * 4
@@ -238,7 +244,7 @@ def cpu_baseline(x, max_threads: int):
     oracle.mla_decode(x.q, x.kv_cache, x.block_table, lens, dtype=x.dtype, softmax_scale=x.softmax_scale,
                       q_scale=x.q_scale, kv_scale=x.kv_scale, num_threads=threads)
     dt = time.perf_counter() - t0
-    e = 1 if x.dtype == 2 else 2
+    e = 1 if x.kv_cache.dtype == np.uint8 else 2
     kv = float(lens.astype(np.int64).sum()) * 576 * e
     return {"value": kv / dt / 1e12, "unit": "TB/s", "cores": threads, "kind": "oracle",
             "sample": f"all {x.B * x.q_len} (sequence, query token) rows of the workload, first {frac:.0%} of each "
@@ -326,15 +332,16 @@ def main():
     print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
     x = mi.workload_inputs(args.workload)
     alg = algorithmic(x)
-    tdt = torch.bfloat16 if x.dtype == mi.BF16 else torch.float8_e4m3fn
-    raw_q = x.q.view(np.int16) if x.dtype == mi.BF16 else x.q
-    raw_kv = x.kv_cache.view(np.int16) if x.dtype == mi.BF16 else x.kv_cache
+    tdt_of = {mi.BF16: torch.bfloat16, mi.FP16: torch.float16, mi.FP8_E4M3: torch.float8_e4m3fn}
+    tq, tdt = tdt_of[mi.q_format(x.dtype)], tdt_of[mi.kv_format(x.dtype)]
+    raw_q = x.q if x.q.dtype == np.uint8 else x.q.view(np.int16)
+    raw_kv = x.kv_cache if x.kv_cache.dtype == np.uint8 else x.kv_cache.view(np.int16)
     kv0 = torch.from_numpy(raw_kv).to(dev).view(tdt)
     pool_bytes = kv0.numel() * kv0.element_size()
     # enough pool copies that a step never finds its KV in the 256 MB cache, capped for tiny pools
     copies = min(64, max(1, math.ceil(3 * MALL_BYTES / pool_bytes)))
     kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
-    q = torch.from_numpy(raw_q).to(dev).view(tdt)
+    q = torch.from_numpy(raw_q).to(dev).view(tq)
     bt = torch.from_numpy(x.block_table).to(dev)
     sl = torch.from_numpy(x.seq_lens).to(dev)
     B, q_len, H = x.B, x.q_len, x.H
@@ -433,7 +440,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(pages_us / (ms_per_step * 1e3), 4) if pages_us else None,
-        "dtype": "fp8_e4m3" if x.dtype == mi.FP8_E4M3 else "bf16",
+        "dtype": DTYPE_NAMES[x.dtype],
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "q_len": q_len, "num_heads": H, "d_qk": 576, "d_v": 512,
                    "page_size": x.page_size, "max_seq_len": x.max_seq_len,
