@@ -64,6 +64,11 @@ hipError_t launch_partial(const PartialParams& p, int dtype, bool fast_pages, hi
 // The merge runs one wave per output row when sequences span few slices on
 // average (G < 16 B), and one workgroup per row otherwise.
 inline bool combine_per_wave(int B, int G) { return (long long)G < 16LL * B; }
+// The 16-bit kernels spread PV over all four waves (the fp8 layout: P through
+// LDS, one more barrier per 32 keys) when a workgroup's 128 rows are not all
+// filled, i.e. fewer than 128 folded rows: otherwise the waves holding rows
+// would do all of PV.  With every row block filled the own-rows layout is faster.
+inline bool cross_wave_pv(int H_eff) { return H_eff < 128; }
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_pack_fp8(const PackParams& p, hipStream_t stream);
 

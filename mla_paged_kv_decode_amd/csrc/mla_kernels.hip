@@ -331,7 +331,8 @@ struct SegmentCtx {
 // result could overflow: the workgroup then recomputes the segment with
 // m_ref set to the exact row maxima seen in the first pass.
 // ---------------------------------------------------------------------------
-template <int DT, bool FAST, bool WIN>
+// XPV (16-bit paths): the fp8 path's cross-wave PV layout instead of the own-rows one.
+template <int DT, bool FAST, bool WIN, bool XPV>
 __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem, int* s_flag, const SegmentCtx& sg,
                                             int g, int mt, int wave, int lane) {
   using TR = Traits<DT>;
@@ -367,12 +368,22 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   const int lim = min(n_row, k1);  // keys [max(k0, lo), lim) are visible to this row
   const int lo = window > 0 ? max(n_row - window, 0) : 0;  // sliding-window start
   // Masking bound of this row, (key - lo) unsigned >= vis for masked keys: below
-  // lo or at/after lim.  With a window it is rebuilt from an opaque copy of
-  // n_row where a tile is masked, so that one value stays live across the loop.
+  // lo or at/after lim.  With a window it is rebuilt where a tile is masked, so
+  // that at most one per-row value stays live across the loop for it: an opaque
+  // copy of n_row (fp8), or none (16-bit paths, whose registers are fuller: n_row
+  // is recomputed from the lane id and uniform values).
   auto mask_bounds = [&](int& lo_m, uint32_t& vis_m) {
     if constexpr (WIN) {
-      int nr = n_row;
-      asm volatile("" : "+v"(nr));
+      int nr;
+      if constexpr (DT == kFp8) {
+        nr = n_row;
+        asm volatile("" : "+v"(nr));
+      } else {
+        int ln = lane, hh_ = p.H;
+        asm volatile("" : "+v"(ln), "+s"(hh_));  // nothing of the division is hoisted out of the loop
+        const int m_ = mt * kTileM + 32 * wave + (ln & 31);
+        nr = m_ < p.H_eff ? min(max(L - p.q_len + gF + m_ / hh_ + 1, 0), L) : 0;
+      }
       lo_m = window > 0 ? max(nr - window, 0) : 0;
       vis_m = (uint32_t)max(min(nr, k1) - lo_m, 0);
     } else {
@@ -423,14 +434,21 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
     // Per-lane DMA geometry: wave instruction kk writes LDS chunk slots
     // [64*(wave+4kk), +64); lane -> slot -> (row, source chunk), kept packed
     // as row << 16 | (row*RB + chunk*16) (that byte offset is below 2^16).
-    uint32_t dgeo[kDmaPerWave];
-#pragma unroll
-    for (int kk = 0; kk < kDmaPerWave; ++kk) {
-      const int slot = 64 * (wave + 4 * kk) + lane;
+    // The nine values stay in registers, except in the cross-wave 16-bit kernels
+    // (twice the Q registers, plus the P exchange) and the bf16-q / E4M3 ones
+    // (widening temporaries), which recompute each one where the load is issued.
+    constexpr bool kGeoRegs = DT == kFp8 || (!XPV && DT != kMixed);
+    auto dma_geo = [&](int kk) -> uint32_t {
+      int ln = lane;
+      if constexpr (!kGeoRegs) asm volatile("" : "+v"(ln));
+      const int slot = 64 * (wave + 4 * kk) + ln;
       const int row = slot / CH;
       const int col = ((slot - row * CH) ^ swz<DT>(row)) * 16;
-      dgeo[kk] = ((uint32_t)row << 16) | (uint32_t)(row * RB + col);
-    }
+      return ((uint32_t)row << 16) | (uint32_t)(row * RB + col);
+    };
+    uint32_t dgeo[kDmaPerWave];
+#pragma unroll
+    for (int kk = 0; kk < kDmaPerWave; ++kk) dgeo[kk] = kGeoRegs ? dma_geo(kk) : 0u;
 
     // fp8: the segment's block-table entries are staged in LDS (kBtEntries at
     // a time, refilled when the tiles run past them) and read from there one
@@ -511,7 +529,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
     };
     // load kk (of kDmaPerWave) of this wave for the tile set up last
     auto dma_issue = [&](int kk) {
-      const uint32_t g = dgeo[kk];
+      const uint32_t g = kGeoRegs ? dgeo[kk] : dma_geo(kk);
       const int row = (int)(g >> 16);
       const uint32_t off = g & 0xffffu;
       const uint32_t m0 = __builtin_amdgcn_readfirstlane(d_m0 + d_step * (uint32_t)(wave + 4 * kk));
@@ -576,8 +594,9 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
       const int grp = lane >> 4, hs = grp >> 1, dsub = grp & 1, uu = lane & 15, rr = uu >> 1, c8 = uu & 1;
       const int kbase = 8 * (rr >> 2) + 4 * hs + (rr & 3);
       const int s8 = (2 * (rr >> 2) + hs) & 3;
-      vaddr[0] = kbase * RB + (((0 + dsub) ^ s8) * 16) + 8 * c8;
-      vaddr[1] = kbase * RB + (((2 + dsub) ^ s8) * 16) + 8 * c8;
+      // (cross-wave PV: + this wave's 128 latent dims, 4 blocks of 32 dims, 2 chunks of 16 bytes each)
+      vaddr[0] = kbase * RB + (((0 + dsub) ^ s8) * 16) + 8 * c8 + (XPV ? 128 * wave : 0);
+      vaddr[1] = kbase * RB + (((2 + dsub) ^ s8) * 16) + 8 * c8 + (XPV ? 128 * wave : 0);
       vaddr[2] = vaddr[3] = 0;
     } else {
       const int sw = swz<DT>(n);
@@ -589,8 +608,8 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         const int sv = ((rr >> 1) << 2) | ((2 * v + hs) & 3);
         const int krow = 8 * v + 4 * hs + rr;
 #pragma unroll
-        for (int x = 0; x < 2; ++x)
-          vaddr[2 * v + x] = krow * RB + (((4 * x + 2 * dsub + (c4 >> 1)) ^ sv) * 16) + 8 * (c4 & 1);
+        for (int x = 0; x < 2; ++x)  // (cross-wave PV: + this wave's 128 latent dims)
+          vaddr[2 * v + x] = krow * RB + (((4 * x + 2 * dsub + (c4 >> 1)) ^ sv) * 16) + 8 * (c4 & 1) + (XPV ? 256 * wave : 0);
       }
     }
 
@@ -985,7 +1004,6 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           }
         };
         float mx_raw = -INFINITY, mref = 0.f, lsum = 0.f;
-        float pvv[16];
         v4i pb[2];
         v16f sc;
         auto sm_chunk = [&](int i, int key0, bool need_mask) {
@@ -1012,21 +1030,116 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             ovf = ovf || (rm > m_ref + kTauOf<DT>);
             mref = m_ref > -INFINITY ? m_ref : 0.f;
           } else if (i >= 2 && i < 6) {
+            // four probabilities, packed at once into the P operand (word 2(g4&1) of pb[g4>>1])
             const int g4 = i - 2;
+            float pv4[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              pvv[4 * g4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * g4 + j], p.s_scale_log2, -mref));
-              lsum += pvv[4 * g4 + j];
+              pv4[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * g4 + j], p.s_scale_log2, -mref));
+              lsum += pv4[j];
             }
-          } else if (i == 6 || i == 7) {
-            const int u = i - 6;
-            pb[u] = v4i{(int)pack_p16x2<CDT>(pvv[8 * u + 0], pvv[8 * u + 1]),
-                        (int)pack_p16x2<CDT>(pvv[8 * u + 2], pvv[8 * u + 3]),
-                        (int)pack_p16x2<CDT>(pvv[8 * u + 4], pvv[8 * u + 5]),
-                        (int)pack_p16x2<CDT>(pvv[8 * u + 6], pvv[8 * u + 7])};
-            if (u == 1) l_acc += lsum;
+            pb[g4 >> 1][2 * (g4 & 1)] = (int)pack_p16x2<CDT>(pv4[0], pv4[1]);
+            pb[g4 >> 1][2 * (g4 & 1) + 1] = (int)pack_p16x2<CDT>(pv4[2], pv4[3]);
+          } else if (i == 7) {
+            l_acc += lsum;
           }
         };
+        if constexpr (XPV) {
+        // PV across the waves, as in the fp8 path: wave w accumulates O^T for latent dims
+        // [128w, 128w+128) of all 128 rows (accumulator 4j + rr: dim block j, row block
+        // rr), so each transposed V read feeds up to four MFMAs.  The row blocks' P
+        // operands (B layout, 1 KiB per 16-key step) pass through LDS.
+        const int nrb = min(4, (p.H_eff - mt * kTileM + 31) / 32);  // row blocks holding rows
+        auto publish_p = [&](const v4i& p0, const v4i& p1) {
+          *(lds_v4i*)(smem + kPOffset + 2048 * wave + 16 * lane) = p0;
+          *(lds_v4i*)(smem + kPOffset + 2048 * wave + 1024 + 16 * lane) = p1;
+        };
+        // Four phases per block (16-key step u, row-block pair h): the phase's two P
+        // operands stay in registers while the wave's four V operands stream past (V is
+        // read twice per block).  The next phase's P operands and first V operand are
+        // read during the current phase, so no phase starts on an LDS wait.
+        auto pread = [&](int u, int rb) -> v4i {
+          return *(const lds_v4i*)(smem + kPOffset + 2048 * rb + 1024 * u + 16 * lane);
+        };
+        auto pv = [&](const lds_t* st, bool with_sm, int key0, bool need_mask) {
+          v4i pk[2] = {pread(0, 0), pread(0, 1)};
+          raw_t an = vread(st, 0, 0);  // vaddr already points at this wave's 128 dims
+#pragma unroll
+          for (int ph = 0; ph < 4; ++ph) {
+            const int u = ph >> 1, h = ph & 1;
+            v4i pn[2] = {pk[0], pk[1]};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const v4i a = ready(an);
+              if (j < 3) {
+                an = vread(st, j + 1, u);
+              } else if (ph < 3) {
+                an = vread(st, 0, (ph + 1) >> 1);
+              }
+              if (j == 1 && ph < 3) {
+                const int un = (ph + 1) >> 1, hn = (ph + 1) & 1;
+                pn[0] = pread(un, 2 * hn);
+                pn[1] = pread(un, 2 * hn + 1);
+              }
+#pragma unroll
+              for (int r2 = 0; r2 < 2; ++r2) {
+                const int rr = 2 * h + r2;
+                if (rr < nrb) o[4 * j + rr] = pv_mfma_h16<CDT>(a, pk[r2], o[4 * j + rr]);
+              }
+              if (with_sm && (j & 1) == 0) sm_chunk(2 * ph + (j >> 1), key0, need_mask);  // one every two steps
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            pk[0] = pn[0];
+            pk[1] = pn[1];
+          }
+        };
+        // score block v covers keys [k0 + 32v, +32) of LDS tile v / HALVES
+        auto block_base = [&](int v) -> const lds_t* {
+          return smem + ((v / HALVES) % kStages) * kStageBytes + (v % HALVES) * CT * RB;
+        };
+        auto block_needs_mask = [&](int key0) { return key0 + CT > lim_min || key0 < lo_max; };
+        const int nblocks = (k1 - k0 + CT - 1) / CT;
+
+        // Block v: [barrier] publish P(v-1); scores of v; [barrier] PV of v-1 with the
+        // softmax of v in its first MFMA slots.  The barrier before the publication
+        // keeps it from overwriting P(v-2) while a wave still reads it.
+        wait_tile_barrier(min(1, ntiles - 1));
+        if (2 < ntiles) issue_tile(2);
+        v4i pp0 = v4i{0, 0, 0, 0}, pp1 = v4i{0, 0, 0, 0};
+        if (wave_active) {
+          qk(smem, sc);
+          const bool nm = block_needs_mask(k0);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sm_chunk(i, k0, nm);
+          pp0 = pb[0];
+          pp1 = pb[1];
+        }
+        for (int v = 1; v < nblocks; ++v) {
+          if (v % HALVES == 0) {
+            const int tt = v / HALVES;
+            wait_tile_barrier(min(1, ntiles - 1 - tt));
+            if (tt + 2 < ntiles) issue_tile(tt + 2);
+          } else {
+            lds_barrier();
+          }
+          if (wave_active) publish_p(pp0, pp1);
+          const int key0 = k0 + v * CT;
+          if (wave_active) qk(block_base(v), sc);
+          lds_barrier();
+          pv(block_base(v - 1), wave_active, key0, block_needs_mask(key0));
+          if (wave_active) {
+            pp0 = pb[0];
+            pp1 = pb[1];
+          }
+        }
+        lds_barrier();
+        if (wave_active) publish_p(pp0, pp1);
+        lds_barrier();
+        pv(block_base(nblocks - 1), false, 0, false);
+              } else {
+        // Own-rows layout: each wave accumulates O^T for its 32 rows x all 512 latent
+        // dims, so no P exchange and no extra barrier (faster when all four row
+        // blocks hold rows).
         auto pv = [&](const lds_t* st, const v4i& p0, const v4i& p1, bool with_sm, int key0, bool need_mask) {
           raw_t vt[kVAhead][2];
 #pragma unroll
@@ -1085,6 +1198,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           pp1 = pb[1];
         }
         if (wave_active) pv(block_base(nblocks - 1), pp0, pp1, false, 0, false);
+              }
       }
       // did any row of the workgroup outgrow its reference?
       const bool wave_ovf = __builtin_amdgcn_ballot_w64(ovf) != 0;
@@ -1097,7 +1211,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   }
 
   // ---- epilogue: normalise, write final or partial ----
-  if constexpr (DT == kFp8) {
+  if constexpr (DT == kFp8 || XPV) {
     // Wave w holds O^T for latent dims [128w, 128w+128) of all 128 rows; the
     // row owners publish 1/l, then the whole 128x512 tile is staged in LDS and
     // written row-contiguous (whole 128-byte lines per store; see store_out for
@@ -1113,10 +1227,11 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
     lds_barrier();  // every wave is done with the KV ring and the P buffer
     if (he == 0) s_inv[32 * wave + ne] = inv;
     lds_barrier();
-    // accumulator rr of every latent block holds row block (wave + rr) & 3
+    // accumulator rr of every latent block holds row block (wave + rr) & 3 (fp8) or rr
+    auto rowblk = [&](int rr) { return DT == kFp8 ? (wave + rr) & 3 : rr; };
     float invr[4];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) invr[rr] = s_inv[32 * ((wave + rr) & 3) + ne];
+    for (int rr = 0; rr < 4; ++rr) invr[rr] = s_inv[32 * rowblk(rr) + ne];
     const bool f32out = !sg.single && !p.part_bf16;
     const int row0 = mt * kTileM;
     if (!f32out) {
@@ -1128,7 +1243,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         for (int rr = 0; rr < 4; ++rr) {
 #pragma unroll
           for (int gq = 0; gq < 4; ++gq) {
-            const int row = 32 * ((wave + rr) & 3) + ne, col = 128 * wave + 32 * j + 8 * gq + 4 * he;
+            const int row = 32 * rowblk(rr) + ne, col = 128 * wave + 32 * j + 8 * gq + 4 * he;
             const v16f& acc = o[4 * j + rr];
             const v2i w = v2i{(int)pack_bf16x2(acc[4 * gq + 0] * invr[rr], acc[4 * gq + 1] * invr[rr]),
                               (int)pack_bf16x2(acc[4 * gq + 2] * invr[rr], acc[4 * gq + 3] * invr[rr])};
@@ -1158,7 +1273,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             for (int rr = 0; rr < 4; ++rr) {
 #pragma unroll
               for (int gq = 0; gq < 4; ++gq) {
-                const int row = 32 * ((wave + rr) & 3) + ne, col = 128 * (wave & 1) + 32 * j + 8 * gq + 4 * he;
+                const int row = 32 * rowblk(rr) + ne, col = 128 * (wave & 1) + 32 * j + 8 * gq + 4 * he;
                 const v16f& acc = o[4 * j + rr];
                 *(__attribute__((address_space(3))) v4f*)(smem + row * kEpiPitch + 4 * col) =
                     v4f{acc[4 * gq + 0] * invr[rr], acc[4 * gq + 1] * invr[rr], acc[4 * gq + 2] * invr[rr],
@@ -1190,7 +1305,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         p.part_lse[(size_t)sg.slot * rows_per_b + rowb] = lse_v;
       }
     }
-  } else {
+    } else {
   // Each wave moves its 32x512 tile through its own LDS region in two passes
   // of 256 columns: accumulators are scaled by 1/l and converted to the
   // output type on the way in (rows padded so the column-wise writes hit
@@ -1270,7 +1385,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   }
 }
 
-template <int DT, bool FAST, bool WIN>
+template <int DT, bool FAST, bool WIN, bool XPV>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_split_kv_partial(PartialParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kLdsBytes];
@@ -1339,7 +1454,7 @@ mla_split_kv_partial(PartialParams p) {
       p.meta[2 * b] = w;
       p.meta[2 * b + 1] = slice_of_unit(P + nb - 1, T, p.G);
     }
-    run_segment<DT, FAST, WIN>(p, smem, s_flag, sg, g, mt, wave, lane);
+    run_segment<DT, FAST, WIN, XPV>(p, smem, s_flag, sg, g, mt, wave, lane);
     cur = seg_end;
     P += nb;
     ++b;
@@ -1573,15 +1688,20 @@ __global__ void __launch_bounds__(256) mla_kv_pack_fp8(PackParams p) {
 
 }  // namespace
 
-template <int DT>
+template <int DT, bool XPV>
 void launch_partial_dt(const PartialParams& p, bool fast_pages, bool win, dim3 grid, dim3 block, hipStream_t stream) {
   if (fast_pages) {
-    if (win) hipLaunchKernelGGL((mla_split_kv_partial<DT, true, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((mla_split_kv_partial<DT, true, false>), grid, block, 0, stream, p);
+    if (win) hipLaunchKernelGGL((mla_split_kv_partial<DT, true, true, XPV>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((mla_split_kv_partial<DT, true, false, XPV>), grid, block, 0, stream, p);
   } else {
-    if (win) hipLaunchKernelGGL((mla_split_kv_partial<DT, false, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((mla_split_kv_partial<DT, false, false>), grid, block, 0, stream, p);
+    if (win) hipLaunchKernelGGL((mla_split_kv_partial<DT, false, true, XPV>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((mla_split_kv_partial<DT, false, false, XPV>), grid, block, 0, stream, p);
   }
+}
+template <int DT>
+void launch_partial_16(const PartialParams& p, bool fast_pages, bool win, dim3 grid, dim3 block, hipStream_t stream) {
+  if (cross_wave_pv(p.H_eff)) launch_partial_dt<DT, true>(p, fast_pages, win, grid, block, stream);
+  else launch_partial_dt<DT, false>(p, fast_pages, win, grid, block, stream);
 }
 
 hipError_t launch_partial(const PartialParams& p, int dtype, bool fast_pages, hipStream_t stream) {
@@ -1590,10 +1710,10 @@ hipError_t launch_partial(const PartialParams& p, int dtype, bool fast_pages, hi
   // window's per-row state costs them no registers
   const bool win = p.window > 0;
   switch (dtype) {
-    case kFp8: launch_partial_dt<kFp8>(p, fast_pages, win, grid, block, stream); break;
-    case kFp16: launch_partial_dt<kFp16>(p, fast_pages, win, grid, block, stream); break;
-    case kMixed: launch_partial_dt<kMixed>(p, fast_pages, win, grid, block, stream); break;
-    default: launch_partial_dt<kBf16>(p, fast_pages, win, grid, block, stream); break;
+    case kFp8: launch_partial_dt<kFp8, true>(p, fast_pages, win, grid, block, stream); break;
+    case kFp16: launch_partial_16<kFp16>(p, fast_pages, win, grid, block, stream); break;
+    case kMixed: launch_partial_16<kMixed>(p, fast_pages, win, grid, block, stream); break;
+    default: launch_partial_16<kBf16>(p, fast_pages, win, grid, block, stream); break;
   }
   return hipGetLastError();
 }

@@ -181,10 +181,11 @@ def test_workspace_errors():
     assert e.value.code == -5
 
 
-def test_hip_graph_replay_matches_eager():
+@pytest.mark.parametrize("dtype", [mi.FP8_E4M3, mi.BF16, mi.FP16, mi.BF16_Q_E4M3_KV])
+def test_hip_graph_replay_matches_eager(dtype):
     """Capture one decode, then replay it with new seq_lens / block_table contents."""
     # every block_table row holds valid pages for 2240 keys; replays use shorter lengths
-    x = mi.make_inputs(3, 4, 32, mi.FP8_E4M3, ("list", [2240, 2240, 2240]), seed=111)
+    x = mi.make_inputs(3, 4, 32, dtype, ("list", [2240, 2240, 2240]), seed=111)
     q, kv, bt, sl = to_dev(x)
     max_len = 2240
     out = torch.empty(3, 4, 32, 512, dtype=torch.bfloat16, device="cuda:0")
@@ -474,6 +475,17 @@ def test_bf16_q_fp8_cache_every_code_widens_exactly():
     for (b, h), d in dims.items():
         assert torch.equal(O[b, 0, h], v_expect), (b, h)
         assert abs(L[b, 0, h] - float(vals[d].float())) <= 1e-6 * max(1.0, abs(float(vals[d].float()))), (b, h, d)
+
+
+# ---------------------------------------------------------------- fewer than 128 folded rows (16-bit paths
+# then spread PV over all four waves, the fp8 path always does)
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP16, mi.BF16_Q_E4M3_KV, mi.FP8_E4M3])
+@pytest.mark.parametrize("H,kw", [(16, {}), (40, {"window": 90}), (96, {"num_splits": 7}), (64, {"no_fold": True})])
+def test_partial_row_tiles(dtype, H, kw):
+    x = mi.make_inputs(3, 1, H, dtype, ("list", [1500, 33, 700]), page_size=64, seed=600 + H)
+    print(f"dtype={dtype} H={H} {kw}", flush=True)
+    out, lse = run_gpu(x, opts=mla.options(**kw) if kw else None)
+    assert_parity(x, out, lse, run_oracle(x, window=kw.get("window", 0)))
 
 
 # ---------------------------------------------------------------- large batches, long pages, short plans
