@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -38,9 +39,17 @@ PAGES_US = {"agentic_b4_q4_h32_fp8_80k": 49.5, "agentic_b16_q4_h32_fp8_80k": 148
 KERNEL_SOURCE = os.path.join(ROOT, "mla_paged_kv_decode_amd", "csrc", "mla_kernels.hip")
 
 
+def code_hash(text: str) -> str:
+    """sha256/16 of HIP source with comments and whitespace removed: edits to comments
+    do not make a profile of the same code stale."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
+
+
 def kernel_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(KERNEL_SOURCE) as f:
+        return code_hash(f.read())
 
 
 def algorithmic(x) -> dict:
@@ -74,7 +83,7 @@ def load_traffic(workload: str):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256_16") != kernel_hash():
+    if t.get("kernel_code_sha256_16") != kernel_hash():
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -167,7 +176,7 @@ def summarize_profile(d: str, workload: str):
     cal_w, _ = _counter_avg(os.path.join(d, "cal_write"), "WRITE_SIZE", "CUDAFunctorOnSelf_add")
     f_scale = COPY_BYTES / (cal_f * 1024.0)
     w_scale = COPY_BYTES / (cal_w * 1024.0)
-    out = {"workload": workload, "kernel_source_sha256_16": kernel_hash(),
+    out = {"workload": workload, "kernel_code_sha256_16": kernel_hash(),
            "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": cal_f, "write_kib": cal_w,
                            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
            "kernels": {}}
@@ -212,7 +221,7 @@ def summarize_profile(d: str, workload: str):
               "| kernel | read MB | written MB |", "|---|---|---|"]
     for k, v in out["kernels"].items():
         lines.append(f"| {k} | {v['fetch_bytes'] / 1e6:.2f} | {v['write_bytes'] / 1e6:.2f} |")
-    lines += ["", f"Kernel source sha256/16: `{out['kernel_source_sha256_16']}`", "", "Commands (repository root):", "",
+    lines += ["", f"Kernel code sha256/16 (comments and whitespace removed): `{out['kernel_code_sha256_16']}`", "", "Commands (repository root):", "",
               "```",
               f"rocprofv3 --kernel-trace --stats -d {d}/trace -o run --output-format csv -- "
               f"python3 bench.py --workload {workload} --steps 50 --warmup 50 --no-cpu-baseline",

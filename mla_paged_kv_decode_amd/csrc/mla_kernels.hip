@@ -2,13 +2,16 @@
 //
 //  * mla_split_kv_partial: one workgroup = 4 waves = 128 folded query rows of
 //    one (sequence, query group) and one contiguous slice of the batch's KV
-//    work.  KV tiles (36,864 bytes: 64 fp8 rows or 32 bf16 rows of 576
-//    elements) stream HBM -> LDS through a 4-deep ring filled by direct
+//    work.  KV tiles (36,864 bytes: 64 E4M3 rows or 32 bf16 / fp16 rows of
+//    576 elements) stream HBM -> LDS through a 4-deep ring filled by direct
 //    global->LDS loads; scores S^T = K Q^T and the output O^T = V^T P^T run on
-//    MFMA (32x32x64 f8f6f4 or 32x32x16 bf16), V^T being read from the same
-//    LDS tile with the transposing LDS reads.  Online softmax in base 2 with a
-//    lazy rescale; the FP8 probabilities carry a per-lane power-of-two block
-//    scale through the MFMA's scale operand.  Writes the final bf16 O / fp32
+//    MFMA (32x32x64 f8f6f4, or 32x32x16 bf16 / f16; bf16 q over an E4M3 cache
+//    widens its K and V operands to bf16 after the LDS read), V^T being read
+//    from the same LDS tile with the transposing LDS reads.  Softmax in base 2
+//    relative to a per-row reference fixed at the row's first visible tile (a
+//    segment is recomputed in the rare case a row max outgrows it); the FP8
+//    probabilities carry a per-row power-of-two block scale through the MFMA's
+//    scale operand.  Writes the final bf16 O / fp32
 //    LSE when the slice holds the whole sequence, else a partial (O, LSE).
 //    (Split-KV partial kernel: TokenSpeed MLA article, section 2; query-token
 //    folding: section 3.)
@@ -42,7 +45,7 @@ typedef __attribute__((address_space(3))) v4i lds_v4i;
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 typedef __attribute__((address_space(4))) const int32_t cint_t;
 
-constexpr float kTau = 32.0f;  // rescale the accumulators only when a row max grows by more (log2 units)
+constexpr float kTau = 32.0f;  // recompute the segment only when a row max grows past the reference by more (log2 units)
 // fp16 P must stay below 65504, so its rows are recomputed once their max grows by more than 2^15
 template <int DT>
 constexpr float kTauOf = DT == kFp16 ? 15.0f : kTau;
@@ -56,9 +59,10 @@ constexpr int kEpiWaveBytes = 32 * kEpiRowF32;
 static_assert(4 * kEpiWaveBytes <= kStages * kStageBytes, "epilogue staging must fit in the KV ring");
 // 1 KiB LDS scratch after the ring: destination of the loads of dummy tiles
 constexpr int kDummyOffset = kStages * kStageBytes;
-// fp8 path: P of the four row blocks (B-operand layout, 2 KiB each) and their
-// per-row MFMA scales (one dword per lane, wave-major so that every access is
-// conflict-free), shared by all waves
+// P exchange of the cross-wave PV layout (fp8 path, and 16-bit kernels with
+// rows missing): P of the four row blocks (B-operand layout, 2 KiB each) and,
+// for fp8, their per-row MFMA scales (one dword per lane, wave-major so that
+// every access is conflict-free), shared by all waves
 constexpr int kPOffset = kDummyOffset + 1024;
 constexpr int kPScaleOffset = kPOffset + 4 * 2048;
 // block-table entries of the current segment, kBtEntries at a time
@@ -207,7 +211,7 @@ __device__ __forceinline__ float xor32_sum(float x) {
 }
 
 // Keep a 16-float accumulator block in AGPRs: values defined by VALU code
-// (zero-init, rescale) are moved there so the loop-carried output tile never
+// (zero-init, the reset before a recomputation) are moved there so the loop-carried output tile never
 // gets a VGPR copy.
 __device__ __forceinline__ void pin_agpr(v16f& x) { asm volatile("" : "+a"(x)); }
 
