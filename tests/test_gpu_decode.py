@@ -489,7 +489,7 @@ def test_partial_row_tiles(dtype, H, kw):
 
 
 # ---------------------------------------------------------------- large batches, long pages, short plans
-@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3, mi.BF16_Q_E4M3_KV])
 @pytest.mark.parametrize("splits", [0, 37])
 def test_large_batch_with_empty_and_short_sequences(dtype, splits):
     """300 sequences (several per lane of the workgroups' prefix sum), zeros and lengths below q_len
