@@ -70,10 +70,10 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int num_cus, const mla_
   pl.m_tiles = (pl.H_eff + mla::kTileM - 1) / mla::kTileM;
   pl.U = pl.q_len_eff * pl.m_tiles;
   pl.part_bf16 = (opt && opt->partial_fp32) ? 0 : 1;
-  long long units_per_seq = max_seq_len > 0 ? (max_seq_len + mla::kUnitKeys - 1) / mla::kUnitKeys : 1;
+  long long units_per_seq = max_seq_len > 0 ? (max_seq_len + mla::kPlanUnitKeys - 1) / mla::kPlanUnitKeys : 1;
   if (opt && opt->window > 0) {
     // a window reads at most window + q_len - 1 keys per sequence, from a unit-aligned start
-    const long long w_units = ((long long)opt->window + q_len - 1 + mla::kUnitKeys - 1) / mla::kUnitKeys + 1;
+    const long long w_units = ((long long)opt->window + q_len - 1 + mla::kPlanUnitKeys - 1) / mla::kPlanUnitKeys + 1;
     if (w_units < units_per_seq) units_per_seq = w_units;
   }
   const long long units_max = (long long)B * units_per_seq;

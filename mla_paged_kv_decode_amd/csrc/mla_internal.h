@@ -11,7 +11,11 @@ namespace mla {
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kTileM = 128;     // folded query rows per workgroup (4 waves x 32 rows)
-constexpr int kUnitKeys = 64;   // keys per work unit of the balanced KV partition
+// Keys per work unit of the host's plan: the smallest LDS tile (32 bf16 / fp16
+// keys), since the plan does not know the dtype.  Each kernel partitions in its
+// own tile (64 keys for E4M3 tiles, whose small batches may then leave some of
+// the planned slices empty: they write nothing and the merge skips them).
+constexpr int kPlanUnitKeys = 32;
 constexpr int kStages = 4;      // LDS ring of KV tiles
 constexpr int kStageBytes = 36864;  // 64 fp8 rows or 32 bf16 rows of 576 elements
 constexpr int kThreads = 256;

@@ -215,18 +215,23 @@ __device__ __forceinline__ float xor32_sum(float x) {
 // gets a VGPR copy.
 __device__ __forceinline__ void pin_agpr(v16f& x) { asm volatile("" : "+a"(x)); }
 
-__device__ __forceinline__ int units_of(int L) { return L > 0 ? (L >> 6) + ((L & 63) != 0) : 1; }
+// Work units of the KV partition are one LDS tile of the kernel: UK = 64 keys
+// (E4M3 tiles) or 32 (16-bit tiles).  A sequence has at least one unit.
+template <int UK>
+__device__ __forceinline__ int units_of(int L) { return L > 0 ? (L + UK - 1) / UK : 1; }
 // First key any query token of a sequence of length L can see, rounded down
-// to a 64-key unit: 0 without a sliding window, else the earliest window start
+// to a unit: 0 without a sliding window, else the earliest window start
 // (token 0's, n_0 - window) rounded down.  The sequence's work is the units
 // from there to L; tiles before it are never read.
+template <int UK>
 __device__ __forceinline__ int seq_key0(int L, int q_len, int window) {
   if (window <= 0) return 0;
   const long long lo = (long long)L - q_len + 1 - window;
-  return lo > 0 ? (int)(lo & ~(long long)(kUnitKeys - 1)) : 0;
+  return lo > 0 ? (int)(lo & ~(long long)(UK - 1)) : 0;
 }
+template <int UK>
 __device__ __forceinline__ int seq_units(int L, int q_len, int window) {
-  return units_of(L - seq_key0(L, q_len, window));
+  return units_of<UK>(L - seq_key0<UK>(L, q_len, window));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -311,7 +316,8 @@ __device__ __forceinline__ void store_out(const v4i& v, v4i* dst, bool final_out
 
 // ---------------------------------------------------------------------------
 // Balanced partition of the batch's KV work: sequence b owns seq_units(L_b)
-// consecutive 64-key units; slice w of G covers units [w*T/G, (w+1)*T/G).
+// consecutive units (one LDS tile each); slice w of G covers units
+// [w*T/G, (w+1)*T/G).
 // Every (slice, sequence) intersection is one segment; its partial lives in
 // workspace slot w + b (unique along the monotone staircase of segments).
 // ---------------------------------------------------------------------------
@@ -358,9 +364,9 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   // keys visible to the last token of this query group
   const int n_gmax = min(max(L - p.q_len + gF + p.F, 0), L);
   const int window = WIN ? p.window : 0;  // sliding window (kernels built without one fold it away)
-  const int kbase = seq_key0(L, p.q_len, window);  // unit 0 of the sequence starts here
-  const int k0 = kbase + sg.u0 * kUnitKeys;
-  const int k1 = min(kbase + sg.u1 * kUnitKeys, n_gmax);
+  const int kbase = seq_key0<TILE>(L, p.q_len, window);  // unit 0 of the sequence starts here
+  const int k0 = kbase + sg.u0 * TILE;
+  const int k1 = min(kbase + sg.u1 * TILE, n_gmax);
 
   // this lane's query row (row n of the wave's 32)
   const int r = 32 * wave + n;
@@ -1395,6 +1401,7 @@ mla_split_kv_partial(PartialParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kLdsBytes];
   __shared__ int s_flag[4];
   lds_t* smem = (lds_t*)smem_raw;
+  constexpr int UK = Traits<DT>::kTile;  // keys per work unit
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases in SGPRs
@@ -1423,7 +1430,7 @@ mla_split_kv_partial(PartialParams p) {
   const int bl0 = min(lane * kper, p.B), bl1 = min(bl0 + kper, p.B);
   long long own = 0;
   const int window = WIN ? p.window : 0;
-  for (int bb = bl0; bb < bl1; ++bb) own += seq_units(p.seq_lens[bb], p.q_len, window);
+  for (int bb = bl0; bb < bl1; ++bb) own += seq_units<UK>(p.seq_lens[bb], p.q_len, window);
   const long long incl = wave_incl_scan_ll(own);
   const long long T = readlane_ll(incl, 63);
   // the merge needs T to recognise empty slices (they write no partials)
@@ -1437,7 +1444,7 @@ mla_split_kv_partial(PartialParams p) {
   long long P = readlane_ll(excl, hl);
   int b = hl * kper;
   while (b + 1 < p.B) {
-    const int nb = seq_units(seq_lens[b], p.q_len, window);
+    const int nb = seq_units<UK>(seq_lens[b], p.q_len, window);
     if (t0 < P + nb) break;
     P += nb;
     ++b;
@@ -1446,7 +1453,7 @@ mla_split_kv_partial(PartialParams p) {
   // ---- segments of this slice ----
   long long cur = t0;
   while (cur < t1 && b < p.B) {
-    const int nb = seq_units(seq_lens[b], p.q_len, window);
+    const int nb = seq_units<UK>(seq_lens[b], p.q_len, window);
     const long long seg_end = min(t1, P + nb);
     SegmentCtx sg;
     sg.b = b;

@@ -63,10 +63,11 @@ def test_plan_fold_factor_and_workspace(B, q_len, H, L, F):
 
 
 def test_plan_small_shapes_spread_one_unit_per_slice():
-    # fewer 64-key units than compute units: one unit per slice (then the merge)
-    assert mla.plan_for_cus(1, 1, 16, 256, 256)[0] == 4
-    assert mla.plan_for_cus(1, 1, 16, 64, 256)[:3:2] == (1, 0)  # one unit: no split, no workspace
-    assert mla.plan_for_cus(2, 1, 16, 300, 256)[0] == 8  # 2 x ceil(300/64) = 10 units, a multiple of 8 from 8 up
+    # fewer 32-key plan units than compute units: one unit per slice (then the merge)
+    assert mla.plan_for_cus(1, 1, 16, 256, 256)[0] == 8
+    assert mla.plan_for_cus(1, 1, 16, 32, 256)[:3:2] == (1, 0)  # one unit: no split, no workspace
+    assert mla.plan_for_cus(1, 1, 16, 64, 256)[0] == 2
+    assert mla.plan_for_cus(2, 1, 16, 300, 256)[0] == 16  # 2 x ceil(300/32) = 20 units, a multiple of 8 from 8 up
     assert mla.plan_for_cus(1, 4, 32, 81920, 256)[0] == 256  # capped by the compute units
 
 
@@ -159,8 +160,8 @@ def test_window_option_validated_and_planned():
     # a window bounds each sequence's work at window + q_len - 1 keys (+ one unit of alignment),
     # so the planned slice count shrinks with it; a window past every length changes nothing
     assert mla.plan_for_cus(1, 4, 32, 81920, 256)[0] == 256
-    assert mla.plan_for_cus(1, 4, 32, 81920, 256, mla.options(window=128))[0] == 4  # ceil(131/64) + 1 units
-    assert mla.plan_for_cus(1, 4, 32, 81920, 256, mla.options(window=1000))[0] == 16  # ceil(1003/64) + 1
+    assert mla.plan_for_cus(1, 4, 32, 81920, 256, mla.options(window=128))[0] == 6  # ceil(131/32) + 1 units
+    assert mla.plan_for_cus(1, 4, 32, 81920, 256, mla.options(window=1000))[0] == 32  # ceil(1003/32) + 1 = 33
     assert mla.plan_for_cus(4, 4, 32, 8192, 256, mla.options(window=100000)) == mla.plan_for_cus(4, 4, 32, 8192, 256)
 
 

@@ -56,13 +56,16 @@ def test_forced_splits(dtype, splits):
 def test_fold_and_partial_precision_options(dtype):
     x = mi.make_inputs(2, 4, 16, dtype, ("list", [1800, 650]), seed=41)
     ref = run_oracle(x)
-    base, lse_b = run_gpu(x)
-    nofold, lse_n = run_gpu(x, opts=mla.options(no_fold=True))
+    planned, lse_0 = run_gpu(x)
+    base, lse_b = run_gpu(x, opts=mla.options(num_splits=24))
+    nofold, lse_n = run_gpu(x, opts=mla.options(no_fold=True, num_splits=24))
     pf32, lse_p = run_gpu(x, opts=mla.options(partial_fp32=True, num_splits=16))
+    assert_parity(x, planned, lse_0, ref)
     assert_parity(x, base, lse_b, ref)
     assert_parity(x, nofold, lse_n, ref)
     assert_parity(x, pf32, lse_p, ref, partial_fp32=True)
-    # folding only re-indexes rows: identical per-row arithmetic
+    # folding only re-indexes rows: with the same split count (the plan's differs, since the
+    # unfolded query groups need more workgroups per slice), identical per-row arithmetic
     assert torch.equal(base, nofold) and torch.equal(lse_b, lse_n)
 
 
