@@ -172,6 +172,33 @@ int mla_decode_ex(const mla_shape* shape, const void* q, const void* kv_cache, c
                   const int32_t* seq_lens, float softmax_scale, float q_scale, float kv_scale, void* out,
                   float* lse, void* workspace, size_t workspace_bytes, void* stream, const mla_options* options);
 
+/*
+ * Ragged batch: sequence b has its own number of new query tokens,
+ * q_len_b = cu_seqlens_q[b+1] - cu_seqlens_q[b], for example a chunked or
+ * ragged varlen prefill over the paged latent cache (tokenspeed-mla package
+ * page and TokenSpeed MLA article, section 1: the varlen ragged prefill
+ * without padding).  Token t of sequence b attends to keys
+ * j < seq_lens[b] - q_len_b + t + 1, the rule of mla_decode with q_len_b in
+ * place of q_len; everything else is as for mla_decode_ex.
+ *
+ *   shape->q_len    the largest q_len_b (it sizes the plan, the fold and the
+ *                   workspace: plan with mla_workspace_bytes_ex(batch, max q_len_b, ...)).
+ *   q               device, [total_q, num_heads, 576]: the new tokens of every
+ *                   sequence, sequence b's at rows [cu_seqlens_q[b], cu_seqlens_q[b+1]).
+ *   cu_seqlens_q    device int32 [batch + 1], non-decreasing, cu_seqlens_q[0] = 0,
+ *                   cu_seqlens_q[batch] = total_q.  Values out of range are clamped into
+ *                   [0, total_q] and counts above shape->q_len are cut to it: no access
+ *                   leaves q, out or lse, but results are then unspecified.
+ *   total_q         host int32, rows of q / out / lse (>= 0; 0 enqueues nothing).
+ *   out, lse        device, [total_q, num_heads, 512] bf16 and [total_q, num_heads] fp32.
+ * Errors: as mla_decode_ex; MLA_ERR_NULL for a NULL cu_seqlens_q, MLA_ERR_SHAPE for
+ * total_q < 0, MLA_ERR_ALIGN for a cu_seqlens_q not 4-byte aligned.
+ */
+int mla_decode_varlen(const mla_shape* shape, const void* q, const int32_t* cu_seqlens_q, int32_t total_q,
+                      const void* kv_cache, const int32_t* block_table, const int32_t* seq_lens, float softmax_scale,
+                      float q_scale, float kv_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream, const mla_options* options);
+
 /* Workspace size and split count for mla_decode_ex with `options` (NULL = defaults). */
 int mla_workspace_bytes_ex(int32_t batch, int32_t q_len, int32_t num_heads, int32_t max_seq_len,
                            const mla_options* options, int32_t* num_splits, size_t* workspace_bytes);

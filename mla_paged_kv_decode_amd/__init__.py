@@ -8,6 +8,7 @@ it every call raises -- there is no fallback implementation.
 Entry points mirror include/mla_decode.h:
   plan(B, q_len, H, max_seq_len)            -> (num_splits, workspace_bytes)
   decode(q, kv_cache, block_table, seq_lens, softmax_scale, ...) -> (out, lse)
+  decode_varlen(q, cu_seqlens_q, kv_cache, block_table, seq_lens, ...) -> (out, lse)
   kv_pack_quantize_fp8(latent, rope, kv_scale, ...) -> uint8 rows [T, 576]
 """
 from __future__ import annotations
@@ -29,8 +30,8 @@ STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_DTYPE", -3: "MLA_ERR_SHA
           -5: "MLA_ERR_WORKSPACE", -6: "MLA_ERR_UNSUPPORTED", -7: "MLA_ERR_HIP", -8: "MLA_ERR_DEVICE"}
 
 # every symbol include/mla_decode.h declares
-EXPORTS = ["mla_get_split_kv_and_workspace", "mla_decode", "mla_decode_ex", "mla_workspace_bytes_ex",
-           "mla_plan_for_cus", "mla_kv_pack_quantize_fp8", "mla_last_error", "mla_version"]
+EXPORTS = ["mla_get_split_kv_and_workspace", "mla_decode", "mla_decode_ex", "mla_decode_varlen",
+           "mla_workspace_bytes_ex", "mla_plan_for_cus", "mla_kv_pack_quantize_fp8", "mla_last_error", "mla_version"]
 
 
 class MlaError(RuntimeError):
@@ -86,13 +87,16 @@ def lib():
     dec = [ctypes.POINTER(MlaShape), p, p, p, p, ctypes.c_float, ctypes.c_float, ctypes.c_float, p, p, p, sz, p]
     L.mla_decode.argtypes = dec
     L.mla_decode_ex.argtypes = dec + [ctypes.POINTER(MlaOptions)]
+    fl = ctypes.c_float
+    L.mla_decode_varlen.argtypes = [ctypes.POINTER(MlaShape), p, p, i32, p, p, p, fl, fl, fl, p, p, p, sz, p,
+                                    ctypes.POINTER(MlaOptions)]
     L.mla_kv_pack_quantize_fp8.argtypes = [p, ctypes.c_int64, p, ctypes.c_int64, p, i32, ctypes.c_float, p,
                                            ctypes.c_int64, p]
     L.mla_last_error.restype = ctypes.c_char_p
     L.mla_last_error.argtypes = []
     L.mla_version.restype = ctypes.c_int
     for f in ("mla_get_split_kv_and_workspace", "mla_workspace_bytes_ex", "mla_plan_for_cus", "mla_decode",
-              "mla_decode_ex", "mla_kv_pack_quantize_fp8"):
+              "mla_decode_ex", "mla_decode_varlen", "mla_kv_pack_quantize_fp8"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -210,6 +214,43 @@ def decode(q, kv_cache, block_table, seq_lens, softmax_scale: float, q_scale: fl
         _check(lib().mla_decode(*args))
     else:
         _check(lib().mla_decode_ex(*args, ctypes.byref(opts)))
+    return out, lse
+
+
+def decode_varlen(q, cu_seqlens_q, kv_cache, block_table, seq_lens, softmax_scale: float, q_scale: float = 1.0,
+                  kv_scale: float = 1.0, *, max_q_len: int, max_seq_len: int, out=None, lse=None, workspace=None,
+                  opts: MlaOptions | None = None, stream=None):
+    """Ragged batch through mla_decode_varlen: sequence b's new tokens are rows
+    [cu_seqlens_q[b], cu_seqlens_q[b+1]) of q [total_q, H, 576]; cu_seqlens_q is a device
+    int32 [B+1]; max_q_len is the largest per-sequence count (host int, sizes the plan).
+    Returns (out bf16 [total_q, H, 512], lse fp32 [total_q, H])."""
+    torch = _torch()
+    if q.dim() != 3 or q.shape[2] != D_QK or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [total_q, H, 576] tensor")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_q.dim() != 1 or not cu_seqlens_q.is_contiguous():
+        raise ValueError("cu_seqlens_q must be a contiguous int32 [B + 1] tensor")
+    B = int(cu_seqlens_q.numel()) - 1
+    q4 = q.view(1, q.shape[0], q.shape[1], D_QK)  # layout checks only
+    _check_layout(q4, kv_cache, block_table, seq_lens)
+    if block_table.shape[0] != B or seq_lens.numel() != B:
+        raise ValueError("block_table and seq_lens must have one row / entry per sequence")
+    total_q, H = int(q.shape[0]), int(q.shape[1])
+    shape = make_shape(q4, kv_cache, block_table, max_seq_len)
+    shape.batch, shape.q_len, shape.num_heads = B, int(max_q_len), H
+    if out is None:
+        out = torch.empty((total_q, H, D_V), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((total_q, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        _, ws_bytes = plan(B, int(max_q_len), H, max_seq_len, opts)
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib().mla_decode_varlen(ctypes.byref(shape), q.data_ptr(), cu_seqlens_q.data_ptr(), total_q,
+                                   kv_cache.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(),
+                                   float(softmax_scale), float(q_scale), float(kv_scale), out.data_ptr(),
+                                   lse.data_ptr(), workspace.data_ptr(), workspace.numel(), stream,
+                                   ctypes.byref(opts) if opts is not None else None))
     return out, lse
 
 

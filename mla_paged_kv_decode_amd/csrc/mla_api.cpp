@@ -161,7 +161,8 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t* bt, const int32_t* seq_lens,
                 float softmax_scale, float q_scale, float kv_scale, void* out, float* lse, void* ws, size_t ws_bytes,
-                void* stream, const mla_options* opt) {
+                void* stream, const mla_options* opt,
+                const int32_t* cu_q = nullptr, int32_t total_q = 0) {
   if (opt && (opt->stages < 0 || opt->stages > 2)) return fail(MLA_ERR_SHAPE, "options.stages must be 0, 1 or 2");
   if (opt && opt->window < 0) return fail(MLA_ERR_SHAPE, "options.window must be >= 0 (got %d)", opt->window);
   if (!s) return fail(MLA_ERR_NULL, "shape is NULL");
@@ -185,6 +186,11 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
   if (!((double)softmax_scale * q_scale * kv_scale > 0.0))
     return fail(MLA_ERR_SHAPE, "softmax_scale * q_scale * kv_scale must be positive");
   if (s->batch == 0) return ok();
+  if (cu_q != nullptr) {  // a ragged batch
+    if (total_q < 0) return fail(MLA_ERR_SHAPE, "total_q must be >= 0 (got %d)", total_q);
+    if (!aligned(cu_q, 4)) return fail(MLA_ERR_ALIGN, "cu_seqlens_q must be 4-byte aligned");
+    if (total_q == 0) return ok();  // no new token anywhere
+  }
   if (!q || !kv || !bt || !seq_lens || !out)
     return fail(MLA_ERR_NULL, "q, kv_cache, block_table, seq_lens and out must be non-NULL");
   if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16))
@@ -240,6 +246,8 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
   p.v_scale = kv_scale;
   p.part_bf16 = pl.part_bf16;
   p.window = opt ? opt->window : 0;
+  p.cu_q = cu_q;
+  p.total_q = total_q;
   const int tile = (dt == mla::kFp8 || dt == mla::kMixed) ? 64 : 32;  // keys per LDS tile
   hipStream_t st = (hipStream_t)stream;
   const int stages = opt ? opt->stages : 0;
@@ -263,6 +271,10 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
     c.rows_per_b = (int)pl.rows_per_b;
     c.G = pl.G;
     c.part_bf16 = pl.part_bf16;
+    c.H = s->num_heads;
+    c.q_len = s->q_len;
+    c.cu_q = cu_q;
+    c.total_q = total_q;
     e = mla::launch_combine(c, st);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch failed: %s", hipGetErrorString(e));
   }
@@ -320,6 +332,15 @@ int mla_decode_ex(const mla_shape* shape, const void* q, const void* kv_cache, c
                   void* workspace, size_t workspace_bytes, void* stream, const mla_options* options) {
   return decode_impl(shape, q, kv_cache, block_table, seq_lens, softmax_scale, q_scale, kv_scale, out, lse, workspace,
                      workspace_bytes, stream, options);
+}
+
+int mla_decode_varlen(const mla_shape* shape, const void* q, const int32_t* cu_seqlens_q, int32_t total_q,
+                      const void* kv_cache, const int32_t* block_table, const int32_t* seq_lens, float softmax_scale,
+                      float q_scale, float kv_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream, const mla_options* options) {
+  if (!cu_seqlens_q) return fail(MLA_ERR_NULL, "cu_seqlens_q is NULL");
+  return decode_impl(shape, q, kv_cache, block_table, seq_lens, softmax_scale, q_scale, kv_scale, out, lse, workspace,
+                     workspace_bytes, stream, options, cu_seqlens_q, total_q);
 }
 
 int mla_kv_pack_quantize_fp8(const void* latent, int64_t latent_stride, const void* rope, int64_t rope_stride,

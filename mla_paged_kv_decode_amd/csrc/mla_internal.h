@@ -41,6 +41,8 @@ struct PartialParams {
   float v_scale;             // kv_scale (V dequantisation)
   int32_t part_bf16;
   int32_t window;            // sliding window in keys (0: none)
+  const int32_t* cu_q;       // ragged batch: [B+1] cumulative new-token counts (device), or nullptr
+  int32_t total_q;           // ragged batch: token rows of q / out
 };
 
 struct CombineParams {
@@ -51,6 +53,9 @@ struct CombineParams {
   float* lse;
   int32_t B, rows_per_b, G;
   int32_t part_bf16;
+  int32_t H, q_len;           // heads and the (largest) query count of a sequence
+  const int32_t* cu_q;        // ragged batch: [B+1] cumulative new-token counts, or nullptr
+  int32_t total_q;
 };
 
 struct PackParams {

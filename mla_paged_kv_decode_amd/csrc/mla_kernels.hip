@@ -341,6 +341,31 @@ struct SegmentCtx {
 // result could overflow: the workgroup then recomputes the segment with
 // m_ref set to the exact row maxima seen in the first pass.
 // ---------------------------------------------------------------------------
+// New query tokens of sequence b, and the index of its first one among q's and
+// out's token rows: q_len each in a uniform batch ([B, q_len, H, ...]), or each
+// sequence's own count from cumulative offsets in a ragged one ([total_q, H,
+// ...]).  Offsets are clamped so that every read stays inside the q tensor.
+__device__ __forceinline__ void seq_tokens(const PartialParams& p, int b, int& qlen_b, int& tok0) {
+  if (p.cu_q == nullptr) {
+    qlen_b = p.q_len;
+    tok0 = b * p.q_len;
+  } else {
+    cint_t* cu = (cint_t*)p.cu_q;
+    const int c0 = min(max(cu[b], 0), p.total_q);
+    const int c1 = min(max(cu[b + 1], c0), p.total_q);
+    tok0 = c0;
+    qlen_b = min(c1 - c0, p.q_len);
+  }
+}
+
+// The query count seq_units needs: only a sliding window makes a sequence's units depend on it.
+__device__ __forceinline__ int units_qlen(const PartialParams& p, int b, int window) {
+  if (window <= 0) return p.q_len;
+  int qlen_b, tok0;
+  seq_tokens(p, b, qlen_b, tok0);
+  return qlen_b;
+}
+
 // XPV (16-bit paths): the fp8 path's cross-wave PV layout instead of the own-rows one.
 template <int DT, bool FAST, bool WIN, bool XPV>
 __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem, int* s_flag, const SegmentCtx& sg,
@@ -360,21 +385,27 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   const int hh = lane >> 5;
   cint_t* seq_lens = (cint_t*)p.seq_lens;
   const int L = max(seq_lens[sg.b], 0);
+  int qlen_b, tok0;
+  seq_tokens(p, sg.b, qlen_b, tok0);
   const int gF = g * p.F;
+  // folded rows that hold a token of this sequence (fewer than H_eff only in the
+  // last query group of a ragged batch's shorter sequences; none past its end)
+  const int rows_valid = min(p.H_eff, max(qlen_b - gF, 0) * p.H);
+  if (rows_valid <= mt * kTileM) return;  // a ragged batch's query group past this sequence's tokens
   // keys visible to the last token of this query group
-  const int n_gmax = min(max(L - p.q_len + gF + p.F, 0), L);
+  const int n_gmax = min(max(L - qlen_b + gF + p.F, 0), L);
   const int window = WIN ? p.window : 0;  // sliding window (kernels built without one fold it away)
-  const int kbase = seq_key0<TILE>(L, p.q_len, window);  // unit 0 of the sequence starts here
+  const int kbase = seq_key0<TILE>(L, qlen_b, window);  // unit 0 of the sequence starts here
   const int k0 = kbase + sg.u0 * TILE;
   const int k1 = min(kbase + sg.u1 * TILE, n_gmax);
 
   // this lane's query row (row n of the wave's 32)
   const int r = 32 * wave + n;
   const int m = mt * kTileM + r;
-  const bool row_valid = m < p.H_eff;
+  const bool row_valid = m < rows_valid;
   const int fold = row_valid ? m / p.H : 0;
   const int t_tok = gF + fold;
-  const int n_row = row_valid ? min(max(L - p.q_len + t_tok + 1, 0), L) : 0;
+  const int n_row = row_valid ? min(max(L - qlen_b + t_tok + 1, 0), L) : 0;
   const int lim = min(n_row, k1);  // keys [max(k0, lo), lim) are visible to this row
   const int lo = window > 0 ? max(n_row - window, 0) : 0;  // sliding-window start
   // Masking bound of this row, (key - lo) unsigned >= vis for masked keys: below
@@ -392,7 +423,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         int ln = lane, hh_ = p.H;
         asm volatile("" : "+v"(ln), "+s"(hh_));  // nothing of the division is hoisted out of the loop
         const int m_ = mt * kTileM + 32 * wave + (ln & 31);
-        nr = m_ < p.H_eff ? min(max(L - p.q_len + gF + m_ / hh_ + 1, 0), L) : 0;
+        nr = m_ < rows_valid ? min(max(L - qlen_b + gF + m_ / hh_ + 1, 0), L) : 0;
       }
       lo_m = window > 0 ? max(nr - window, 0) : 0;
       vis_m = (uint32_t)max(min(nr, k1) - lo_m, 0);
@@ -401,8 +432,9 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
       vis_m = (uint32_t)lim;
     }
   };
-  const size_t rows_per_b = (size_t)p.q_len * p.H;
-  const bool wave_active = (mt * kTileM + 32 * wave) < p.H_eff;
+  const size_t rows_per_b = (size_t)p.q_len * p.H;  // rows of a sequence's workspace slot
+  const size_t out_row0 = (size_t)tok0 * p.H;       // the sequence's first row of out / lse
+  const bool wave_active = (mt * kTileM + 32 * wave) < rows_valid;
 
   // ---- Q rows into registers, laid out as the B operand of S^T = K Q^T ----
   // (invalid rows read row 0 of the group and are zeroed: no divergent branches)
@@ -411,7 +443,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   constexpr int QSTEPS = (DT == kFp8) ? 9 : 36;
   v8i qreg[QSTEPS];
   if constexpr (DT != kFp8) {
-    const size_t qrow_idx = ((size_t)sg.b * p.q_len + gF) * p.H + (size_t)(row_valid ? m : 0);
+    const size_t qrow_idx = ((size_t)tok0 + gF) * p.H + (size_t)(row_valid ? m : 0);
     const uint8_t* qrow = p.q + qrow_idx * kDqk * ESZ;
     const int keep = row_valid ? -1 : 0;
 #pragma unroll
@@ -896,7 +928,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         // until tile 2 is issued, so their latency overlaps that of tiles 0-1.
         constexpr int kQDma = 32 * kDqk / 1024;  // 18 one-KiB loads per wave
         {
-          const uint8_t* qblk = p.q + ((size_t)sg.b * p.q_len + gF) * p.H * kDqk;
+          const uint8_t* qblk = p.q + ((size_t)tok0 + gF) * p.H * kDqk;
           const uint32_t qlds = smem_base + (uint32_t)(2 * kStageBytes + wave * 32 * kDqk);
           int qlane = lane;
           asm volatile("" : "+v"(qlane));  // addresses computed here, not kept live from the segment start
@@ -905,7 +937,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             const int o = 1024 * kk + 16 * qlane;
             const int qn = o / kDqk;
             const int mrow = mt * kTileM + 32 * wave + qn;
-            const int src_row = mrow < p.H_eff ? mrow : 0;
+            const int src_row = mrow < rows_valid ? mrow : 0;
             dma16_vaddr(qblk + (size_t)src_row * kDqk + (o - qn * kDqk),
                         __builtin_amdgcn_readfirstlane(qlds + 1024u * (uint32_t)kk));
           }
@@ -1059,7 +1091,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         // [128w, 128w+128) of all 128 rows (accumulator 4j + rr: dim block j, row block
         // rr), so each transposed V read feeds up to four MFMAs.  The row blocks' P
         // operands (B layout, 1 KiB per 16-key step) pass through LDS.
-        const int nrb = min(4, (p.H_eff - mt * kTileM + 31) / 32);  // row blocks holding rows
+        const int nrb = min(4, (rows_valid - mt * kTileM + 31) / 32);  // row blocks holding rows
         auto publish_p = [&](const v4i& p0, const v4i& p1) {
           *(lds_v4i*)(smem + kPOffset + 2048 * wave + 16 * lane) = p0;
           *(lds_v4i*)(smem + kPOffset + 2048 * wave + 1024 + 16 * lane) = p1;
@@ -1245,7 +1277,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
     const bool f32out = !sg.single && !p.part_bf16;
     const int row0 = mt * kTileM;
     if (!f32out) {
-      uint16_t* dst = sg.single ? p.out + (size_t)sg.b * rows_per_b * kDv
+      uint16_t* dst = sg.single ? p.out + out_row0 * kDv
                                 : (uint16_t*)p.part_o + (size_t)sg.slot * rows_per_b * kDv;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -1267,7 +1299,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         const int row = 32 * wave + k;
         const v4i v = *(const lds_v4i*)(smem + row * kEpiPitch + 16 * lane);
         const int m_r = row0 + row;
-        if (m_r < p.H_eff) {
+        if (m_r < rows_valid) {
           const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
           store_out(v, (v4i*)(dst + rowb * kDv + 8 * lane), sg.single);
         }
@@ -1298,7 +1330,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           const int row = 32 * wave + k;
           const v4f v = *(const __attribute__((address_space(3))) v4f*)(smem + row * kEpiPitch + 16 * lane);
           const int m_r = row0 + row;
-          if (m_r < p.H_eff) {
+          if (m_r < rows_valid) {
             const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
             *(v4f*)(dst + rowb * kDv + 256 * h + 4 * lane) = v;  // a partial: the merge reads it next
           }
@@ -1307,10 +1339,10 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
       }
     }
     const int m_l = row0 + 32 * wave + ne;
-    if (m_l < p.H_eff && he == 0) {
+    if (m_l < rows_valid && he == 0) {
       const size_t rowb = (size_t)gF * p.H + (size_t)m_l;
       if (sg.single) {
-        if (p.lse != nullptr) p.lse[(size_t)sg.b * rows_per_b + rowb] = lse_v;
+        if (p.lse != nullptr) p.lse[out_row0 + rowb] = lse_v;
       } else {
         p.part_lse[(size_t)sg.slot * rows_per_b + rowb] = lse_v;
       }
@@ -1332,7 +1364,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   lds_barrier();  // every wave is done with the KV ring
   lds_t* wl = smem + wave * kEpiWaveBytes;
   if (!f32out) {
-    uint16_t* dst = sg.single ? p.out + (size_t)sg.b * rows_per_b * kDv
+    uint16_t* dst = sg.single ? p.out + out_row0 * kDv
                               : (uint16_t*)p.part_o + (size_t)sg.slot * rows_per_b * kDv;
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
@@ -1352,7 +1384,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         const int r = 2 * k + (lane >> 5), ch = lane & 31;
         const v4i v = *(const lds_v4i*)(wl + r * kEpiRowB16 + 16 * ch);
         const int m_r = wrow0 + r;
-        if (m_r < p.H_eff) {
+        if (m_r < rows_valid) {
           const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
           store_out(v, (v4i*)(dst + rowb * kDv + 256 * pass + 8 * ch), sg.single);
         }
@@ -1376,7 +1408,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
       for (int r = 0; r < 32; ++r) {
         const v4f v = *(const __attribute__((address_space(3))) v4f*)(wl + r * kEpiRowF32 + 16 * lane);
         const int m_r = wrow0 + r;
-        if (m_r < p.H_eff) {
+        if (m_r < rows_valid) {
           const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
           *(v4f*)(dst + rowb * kDv + 256 * pass + 4 * lane) = v;  // a partial: the merge reads it next
         }
@@ -1384,10 +1416,10 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
     }
   }
   const int m_l = wrow0 + ne;
-  if (m_l < p.H_eff && he == 0) {
+  if (m_l < rows_valid && he == 0) {
     const size_t rowb = (size_t)gF * p.H + (size_t)m_l;
     if (sg.single) {
-      if (p.lse != nullptr) p.lse[(size_t)sg.b * rows_per_b + rowb] = lse_v;
+      if (p.lse != nullptr) p.lse[out_row0 + rowb] = lse_v;
     } else {
       p.part_lse[(size_t)sg.slot * rows_per_b + rowb] = lse_v;
     }
@@ -1430,7 +1462,7 @@ mla_split_kv_partial(PartialParams p) {
   const int bl0 = min(lane * kper, p.B), bl1 = min(bl0 + kper, p.B);
   long long own = 0;
   const int window = WIN ? p.window : 0;
-  for (int bb = bl0; bb < bl1; ++bb) own += seq_units<UK>(p.seq_lens[bb], p.q_len, window);
+  for (int bb = bl0; bb < bl1; ++bb) own += seq_units<UK>(p.seq_lens[bb], units_qlen(p, bb, window), window);
   const long long incl = wave_incl_scan_ll(own);
   const long long T = readlane_ll(incl, 63);
   // the merge needs T to recognise empty slices (they write no partials)
@@ -1444,7 +1476,7 @@ mla_split_kv_partial(PartialParams p) {
   long long P = readlane_ll(excl, hl);
   int b = hl * kper;
   while (b + 1 < p.B) {
-    const int nb = seq_units<UK>(seq_lens[b], p.q_len, window);
+    const int nb = seq_units<UK>(seq_lens[b], units_qlen(p, b, window), window);
     if (t0 < P + nb) break;
     P += nb;
     ++b;
@@ -1453,7 +1485,7 @@ mla_split_kv_partial(PartialParams p) {
   // ---- segments of this slice ----
   long long cur = t0;
   while (cur < t1 && b < p.B) {
-    const int nb = seq_units<UK>(seq_lens[b], p.q_len, window);
+    const int nb = seq_units<UK>(seq_lens[b], units_qlen(p, b, window), window);
     const long long seg_end = min(t1, P + nb);
     SegmentCtx sg;
     sg.b = b;
@@ -1472,6 +1504,22 @@ mla_split_kv_partial(PartialParams p) {
   }
 }
 
+// Row `row` of sequence b's workspace slot -> its row of out / lse.  In a ragged
+// batch the rows past the sequence's tokens hold nothing (false); the offsets are
+// clamped exactly as the split-KV kernel clamps them.
+__device__ __forceinline__ bool merge_out_row(const CombineParams& p, int b, int row, size_t& orow) {
+  if (p.cu_q == nullptr) {
+    orow = (size_t)b * p.rows_per_b + row;
+    return true;
+  }
+  cint_t* cu = (cint_t*)p.cu_q;
+  const int c0 = min(max(cu[b], 0), p.total_q);
+  const int c1 = min(max(cu[b + 1], c0), p.total_q);
+  if (row >= min(c1 - c0, p.q_len) * p.H) return false;
+  orow = (size_t)c0 * p.H + row;
+  return true;
+}
+
 // ---------------------------------------------------------------------------
 // Merge: one workgroup per output row.  The slice weights exp(lse_s - LSE)
 // are computed once per row into LDS (256 slices at a time); each of the four
@@ -1486,6 +1534,8 @@ __global__ void __launch_bounds__(256) mla_combine(CombineParams p) {
   if (grow >= (long long)p.B * p.rows_per_b) return;
   const int b = (int)(grow / p.rows_per_b);
   const int row = (int)(grow - (long long)b * p.rows_per_b);
+  size_t orow;
+  if (!merge_out_row(p, b, row, orow)) return;
   const int w0 = max(p.meta[2 * b], 0), w1 = min(p.meta[2 * b + 1], p.G - 1);
   if (w0 >= w1) return;  // single slice: written by the partial kernel
   // slices that hold no work (more slices than units) wrote nothing: weight 0
@@ -1552,8 +1602,8 @@ __global__ void __launch_bounds__(256) mla_combine(CombineParams p) {
       }
     }
   }
-  *(uint32_t*)(p.out + ((size_t)b * p.rows_per_b + row) * kDv + d) = pack_bf16x2(acc0, acc1);
-  if (p.lse != nullptr && tid == 0) p.lse[(size_t)b * p.rows_per_b + row] = lse_out;
+  *(uint32_t*)(p.out + orow * kDv + d) = pack_bf16x2(acc0, acc1);
+  if (p.lse != nullptr && tid == 0) p.lse[orow] = lse_out;
 }
 
 // ---------------------------------------------------------------------------
@@ -1569,6 +1619,8 @@ __global__ void __launch_bounds__(256) mla_combine_rows(CombineParams p) {
   if (grow >= (long long)p.B * p.rows_per_b) return;
   const int b = (int)(grow / p.rows_per_b);
   const int row = (int)(grow - (long long)b * p.rows_per_b);
+  size_t orow;
+  if (!merge_out_row(p, b, row, orow)) return;
   const int w0 = max(p.meta[2 * b], 0), w1 = min(p.meta[2 * b + 1], p.G - 1);
   if (w0 >= w1) return;  // single slice: written by the partial kernel
   const int n = w1 - w0 + 1;
@@ -1644,8 +1696,8 @@ __global__ void __launch_bounds__(256) mla_combine_rows(CombineParams p) {
   }
   const v4i packed = v4i{(int)pack_bf16x2(acc[0], acc[1]), (int)pack_bf16x2(acc[2], acc[3]),
                          (int)pack_bf16x2(acc[4], acc[5]), (int)pack_bf16x2(acc[6], acc[7])};
-  *(v4i*)(p.out + ((size_t)b * p.rows_per_b + row) * kDv + 8 * lane) = packed;
-  if (p.lse != nullptr && lane == 0) p.lse[(size_t)b * p.rows_per_b + row] = lse_out;
+  *(v4i*)(p.out + orow * kDv + 8 * lane) = packed;
+  if (p.lse != nullptr && lane == 0) p.lse[orow] = lse_out;
 }
 
 // ---------------------------------------------------------------------------

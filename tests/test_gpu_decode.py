@@ -4,6 +4,7 @@ Tolerances: bf16 O max-abs <= 1e-2, LSE <= 1e-3; FP8 O <= 5e-2 (the oracle
 runs on the dequantised FP8 values), LSE <= 1e-3.  Index handling (paging,
 masking, needles, page relabelling) is checked bit-exactly.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -522,3 +523,95 @@ def test_lengths_above_the_planned_maximum():
     out, lse = mla.decode(q, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_seq_len=100)
     torch.cuda.synchronize()
     assert_parity(x, out, lse, run_oracle(x))
+
+
+# ---------------------------------------------------------------- many new tokens per sequence (prefill-sized q_len)
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+@pytest.mark.parametrize("B,q_len,H,lens", [(2, 96, 16, [700, 300]), (1, 256, 8, [1024]), (2, 60, 32, [60, 2000])])
+def test_prefill_sized_query_counts(dtype, B, q_len, H, lens):
+    """q_len in the hundreds: the causal mask runs across the new tokens, folded groups stream
+    only the keys they can see (sequences as long as q_len see no cached prefix at all)."""
+    x = mi.make_inputs(B, q_len, H, dtype, ("list", lens), page_size=64, seed=700 + q_len + H)
+    print(f"dtype={dtype} B={B} q_len={q_len} H={H} lens={lens}", flush=True)
+    out, lse = run_gpu(x)
+    assert_parity(x, out, lse, run_oracle(x))
+
+
+# ---------------------------------------------------------------- ragged batches: each sequence its own query count
+def _ragged(x, q_lens, dev="cuda:0"):
+    """Sequence b keeps the first q_lens[b] of the max(q_lens) query tokens drawn for it; returns
+    the packed device tensors and the fp64 reference, one oracle call per sequence."""
+    from tests.gpu_util import _torch_dtype
+    qf = mi.q_format(x.dtype)
+    rows = [x.q[b, :ql] for b, ql in enumerate(q_lens)]
+    q_pack = np.ascontiguousarray(np.concatenate(rows, axis=0))  # [total_q, H, 576]
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    raw = q_pack if qf == mi.FP8_E4M3 else q_pack.view(np.int16)
+    q = torch.from_numpy(raw).to(dev).view(_torch_dtype(qf))
+    O, L, A = [], [], []
+    for b, ql in enumerate(q_lens):
+        if ql == 0:
+            continue
+        sub = dataclasses.replace(x, q=np.ascontiguousarray(x.q[b:b + 1, :ql]), block_table=x.block_table[b:b + 1],
+                                  seq_lens=x.seq_lens[b:b + 1])
+        o, l, a = run_oracle(sub, window=0)
+        O.append(o[0]), L.append(l[0]), A.append(a[0])
+    H = x.q.shape[2]
+    ref = tuple(np.concatenate(v, axis=0) if v else np.zeros((0, H, 512) if i != 1 else (0, H))
+                for i, v in enumerate((O, L, A)))
+    return q, torch.from_numpy(cu).to(dev), ref
+
+
+RAGGED_CASES = [
+    # dtype, H, q_lens, lens, options
+    (mi.BF16, 16, [1, 7, 0, 33], [300, 7, 40, 2000], {}),
+    (mi.FP8_E4M3, 32, [4, 1, 3, 4], [81920 // 64, 100, 2, 700], {}),
+    (mi.BF16_Q_E4M3_KV, 16, [12, 5, 1], [900, 5, 3000], {"num_splits": 40}),
+    (mi.FP16, 128, [2, 9, 1], [1500, 300, 64], {}),
+    (mi.FP8_E4M3, 64, [6, 2, 5, 1, 6], [700, 1, 1300, 64, 6], {"partial_fp32": True}),
+]
+
+
+@pytest.mark.parametrize("dtype,H,q_lens,lens,kw", RAGGED_CASES)
+def test_ragged_query_counts(dtype, H, q_lens, lens, kw):
+    x = mi.make_inputs(len(q_lens), max(q_lens), H, dtype, ("list", lens), page_size=64, seed=800 + H + len(q_lens))
+    print(f"dtype={dtype} H={H} q_lens={q_lens} lens={lens} {kw}", flush=True)
+    q, cu, ref = _ragged(x, q_lens)
+    kv, bt, sl = to_dev(x)[1:]
+    opts = mla.options(**kw) if kw else None
+    out, lse = mla.decode_varlen(q, cu, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale,
+                                 max_q_len=max(q_lens), max_seq_len=x.max_seq_len, opts=opts)
+    torch.cuda.synchronize()
+    assert_parity(x, out, lse, ref, partial_fp32=bool(kw.get("partial_fp32", False)))
+
+
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+def test_ragged_entry_with_equal_counts_matches_decode(dtype):
+    """Equal counts through the ragged entry point: the same kernels and plan, bit-identical."""
+    x = mi.make_inputs(3, 4, 32, dtype, ("list", [1000, 77, 2500]), seed=811)
+    q4, kv, bt, sl = to_dev(x)
+    out_u, lse_u = run_gpu(x, tensors=(q4, kv, bt, sl))
+    cu = torch.arange(0, 13, 4, dtype=torch.int32, device="cuda:0")
+    out_r, lse_r = mla.decode_varlen(q4.reshape(12, 32, 576), cu, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale,
+                                     max_q_len=4, max_seq_len=x.max_seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(out_r.view(3, 4, 32, 512), out_u) and torch.equal(lse_r.view(3, 4, 32), lse_u)
+
+
+def test_ragged_window_and_more_tokens_than_keys():
+    """A sliding window over a ragged batch whose sequences hold fewer keys than new tokens."""
+    q_lens, lens = [8, 3, 8], [5, 900, 1200]
+    x = mi.make_inputs(3, 8, 16, mi.BF16, ("list", lens), page_size=16, seed=821)
+    q, cu, _ = _ragged(x, q_lens)
+    O, L, A = [], [], []
+    for b, ql in enumerate(q_lens):
+        sub = dataclasses.replace(x, q=np.ascontiguousarray(x.q[b:b + 1, :ql]), block_table=x.block_table[b:b + 1],
+                                  seq_lens=x.seq_lens[b:b + 1])
+        o, l, a = run_oracle(sub, window=50)
+        O.append(o[0]), L.append(l[0]), A.append(a[0])
+    ref = tuple(np.concatenate(v, axis=0) for v in (O, L, A))
+    kv, bt, sl = to_dev(x)[1:]
+    out, lse = mla.decode_varlen(q, cu, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_q_len=8,
+                                 max_seq_len=x.max_seq_len, opts=mla.options(window=50, num_splits=9))
+    torch.cuda.synchronize()
+    assert_parity(x, out, lse, ref)
