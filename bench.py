@@ -301,6 +301,73 @@ def bench_pack(args):
                                    "algorithmic_bytes_per_launch": nbytes}}), flush=True)
 
 
+def bench_ragged(args):
+    """mla_decode_varlen on a ragged prefill: every sequence's new tokens attend causally to its
+    cached keys and to each other.  MFMA-bound: each key row serves many query rows."""
+    import numpy as np
+    import torch
+
+    import mla_inputs as mi
+    import mla_paged_kv_decode_amd as mla
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    x, new = mi.ragged_prefill_inputs(args.workload)
+    ctx = mi.RAGGED_PREFILL[args.workload]["ctx"]
+    H, dtype = x.H, x.dtype
+    lens = [int(v) for v in x.seq_lens]
+    B, max_new = len(new), max(new)
+    q_pack = np.ascontiguousarray(np.concatenate([x.q[b, :n] for b, n in enumerate(new)], axis=0))
+    tdt = torch.float8_e4m3fn if dtype == mi.FP8_E4M3 else torch.bfloat16
+    raw = (lambda a: a if a.dtype == np.uint8 else a.view(np.int16))
+    q = torch.from_numpy(raw(q_pack)).to(dev).view(tdt)
+    kv = torch.from_numpy(raw(x.kv_cache)).to(dev).view(tdt)
+    bt = torch.from_numpy(x.block_table).to(dev)
+    sl = torch.from_numpy(x.seq_lens).to(dev)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(new)]).astype(np.int32), device=dev)
+    total_q = int(sum(new))
+    out = torch.empty(total_q, H, 512, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(total_q, H, dtype=torch.float32, device=dev)
+    G, ws_bytes = mla.plan(B, max_new, H, x.max_seq_len)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def timed(stages):
+        opts = mla.options(stages=stages)
+        run = lambda: mla.decode_varlen(q, cu, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_q_len=max_new,
+                                        max_seq_len=x.max_seq_len, out=out, lse=lse, workspace=ws, opts=opts)
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms = timed(0)
+    part = timed(1)
+    vis = sum(max(0, min(L - n + t + 1, L)) for L, n in zip(lens, new) for t in range(n))
+    flops = 2 * (576 + 512) * H * vis
+    e = 1 if dtype == mi.FP8_E4M3 else 2
+    nbytes = sum(lens) * 576 * e + total_q * H * (576 * e + 512 * 2 + 4)
+    peak = MFMA_PEAK_TFLOPS[dtype]
+    tfs = flops / (part * 1e-3) / 1e12
+    print(json.dumps({"metric": "ragged prefill over the paged latent cache (mla_decode_varlen)",
+                      "value": round(flops / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s", "n_gpus": 1,
+                      "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+                      "us_per_step": round(ms * 1e3, 2), "higher_is_better": True, "dtype": DTYPE_NAMES[dtype],
+                      "data": "synthetic",
+                      "config": {"workload": args.workload, "new_tokens": new, "cached_keys": ctx, "num_heads": H,
+                                 "num_splits": G, "page_size": 64},
+                      "roofline": {"bound": "mfma", "kernel": "mla_split_kv_partial", "achieved": round(tfs, 1),
+                                   "peak": peak, "unit": "TFLOP/s", "frac": round(tfs / peak, 4),
+                                   "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,
+                                   "avg_launch_ms": round(part, 5)},
+                      "kernels_ms": {"split_kv_partial": round(part, 5)}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -328,6 +395,9 @@ def main():
         sys.exit(2)
     if args.pack_tokens > 0:
         bench_pack(args)
+        return
+    if args.workload.startswith("ragged_prefill"):
+        bench_ragged(args)
         return
 
     import numpy as np

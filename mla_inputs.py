@@ -235,6 +235,23 @@ def workload_inputs(name: str, seed=None, **overrides) -> DecodeInputs:
     return make_inputs(w["B"], w["q_len"], w["H"], w["dtype"], w["lens"], **kw)
 
 
+# Ragged prefill workloads (the pages name a varlen ragged prefill but give no shapes): sequence b
+# gets new[b] new tokens over ctx[b] cached keys, so seq_lens = ctx + new.
+RAGGED_PREFILL = {
+    "ragged_prefill_b4_h16_fp8": dict(H=16, dtype=FP8_E4M3, new=[512, 1024, 256, 768], ctx=[8192, 4096, 16384, 2048]),
+    "ragged_prefill_b4_h128_bf16": dict(H=128, dtype=BF16, new=[128, 512, 64, 256], ctx=[8192, 4096, 16384, 2048]),
+}
+
+
+def ragged_prefill_inputs(name: str, seed: int = 1100):
+    """(inputs of a uniform batch of max(new) tokens, new): sequence b keeps its first new[b] tokens."""
+    w = RAGGED_PREFILL[name]
+    lens = [c + n for c, n in zip(w["ctx"], w["new"])]
+    x = make_inputs(len(lens), max(w["new"]), w["H"], w["dtype"], ("list", lens), page_size=64, seed=seed,
+                    spare_pages=64, name=name)
+    return x, list(w["new"])
+
+
 def workload_lens(name: str, seed=None) -> np.ndarray:
     """Only the sequence lengths of a workload (first draw of its stream)."""
     w = WORKLOADS[name]

@@ -206,3 +206,18 @@ def test_dtype_pairs_of_the_binding():
         mla._pair_code(f8.view(64, 1, 1, 576), bf)  # fp8 q over a bf16 cache is not a supported pair
     with pytest.raises(TypeError):
         mla._pair_code(bf, h)
+
+
+def test_varlen_validation_without_device():
+    L = mla.lib()
+    shape = _shape()
+
+    def call(cu=16, total_q=8, q=16):
+        return L.mla_decode_varlen(ctypes.byref(shape), q, cu, total_q, 16, 16, 16, 1.0, 1.0, 1.0, 16, None, None, 0,
+                                   None, None)
+
+    assert call(cu=None) == -1 and b"cu_seqlens_q" in L.mla_last_error()
+    assert call(total_q=-1) == -3
+    assert call(cu=18) == -4
+    assert call(total_q=0) == 0  # no new token anywhere: nothing enqueued
+    assert call(q=None) == -1

@@ -65,3 +65,35 @@ def test_workload_parity(name):
         print(f"    sequence {b} (L={int(x.seq_lens[b])}): oracle {time.time() - t1:.1f} s", flush=True)
 
         assert_parity(sub, torch.from_numpy(O[b:b + 1]), torch.from_numpy(L[b:b + 1]), ref, flat=True)
+
+
+@pytest.mark.parametrize("name", list(mi.RAGGED_PREFILL))
+def test_ragged_prefill_workload(name):
+    """The ragged prefill workloads bench.py times, at full size through mla_decode_varlen: the
+    whole output is finite, and the sequence with the fewest new tokens (every one of its
+    tokens and heads) matches the fp64 oracle."""
+    from tests.gpu_util import _torch_dtype
+    x, new = mi.ragged_prefill_inputs(name)
+    qf = mi.q_format(x.dtype)
+    q_pack = np.ascontiguousarray(np.concatenate([x.q[b, :n] for b, n in enumerate(new)], axis=0))
+    raw = q_pack if q_pack.dtype == np.uint8 else q_pack.view(np.int16)
+    q = torch.from_numpy(raw).to("cuda:0").view(_torch_dtype(qf))
+    _, kv, bt, sl = to_dev(x)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(new)]).astype(np.int32), device="cuda:0")
+    out, lse = mla.decode_varlen(q, cu, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_q_len=max(new),
+                                 max_seq_len=x.max_seq_len)
+    torch.cuda.synchronize()
+    O = out_f64(out)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse.cpu().numpy()))
+    b = int(np.argmin(new))
+    t1 = time.time()
+    sub = dataclasses.replace(x, q=np.ascontiguousarray(x.q[b:b + 1, :new[b]]), block_table=x.block_table[b:b + 1],
+                              seq_lens=x.seq_lens[b:b + 1])
+    ref = oracle.mla_decode(sub.q, sub.kv_cache, sub.block_table, sub.seq_lens, dtype=x.dtype,
+                            softmax_scale=x.softmax_scale, q_scale=x.q_scale, kv_scale=x.kv_scale, want_absv=True,
+                            num_threads=16)
+    print(f"    {name}: sequence {b} ({new[b]} new tokens, L={int(x.seq_lens[b])}): oracle {time.time() - t1:.1f} s",
+          flush=True)
+    r0 = int(np.sum(new[:b]))
+    assert_parity(sub, torch.from_numpy(O[r0:r0 + new[b]][None]), lse[r0:r0 + new[b]][None].cpu(),
+                  ref, flat=True)
