@@ -38,12 +38,19 @@ int ok() {
 // small batch is faster spread one unit per slice plus the merge (256 keys of
 // bf16: 22 us) than run as fewer, longer slices (28 us as one slice).
 constexpr int kMinUnitsPerSlice = 1;
+// Above this many workgroup rows (query groups x row tiles) the rows' work can
+// differ widely: the query groups of a ragged batch hold tokens of different
+// sequences, and causal groups of a long query see different key counts.
+// Such launches take about kDynamicWaves workgroups per compute unit, so the
+// hardware dispatcher evens out the rows instead of a static one-per-CU cut.
+constexpr int kManyRows = 32;
+constexpr int kDynamicWaves = 4;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
-  int F, H_eff, q_len_eff, m_tiles, U, G, xcd_map, part_bf16;
+  int F, H_eff, q_len_eff, m_tiles, U, G, xcd_map, u_major, part_bf16;
   size_t rows_per_b;
   size_t off_part_o, off_part_lse, off_meta, bytes;
 };
@@ -59,9 +66,10 @@ int fold_factor(int q_len, int H, bool no_fold) {
 }
 
 // Split heuristic: one workgroup per compute unit (each holds a 147 KiB LDS
-// ring and 512 VGPRs per lane), the batch's KV work cut into G equal slices,
-// none smaller than kMinUnitsPerSlice 64-key units.  G is a multiple of 8
-// when >= 8 so every XCD gets the same number of slices.
+// ring and 512 VGPRs per lane), each workgroup row's KV work cut into G equal
+// slices, none smaller than kMinUnitsPerSlice units; with more than kManyRows
+// rows, about kDynamicWaves workgroups per compute unit instead.  G is a
+// multiple of 8 when >= 8 so every XCD gets the same number of slices.
 Plan make_plan(int B, int q_len, int H, int max_seq_len, int num_cus, const mla_options* opt) {
   Plan pl{};
   pl.F = fold_factor(q_len, H, opt && opt->no_fold);
@@ -81,7 +89,7 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int num_cus, const mla_
   if (opt && opt->num_splits > 0) {
     G = opt->num_splits;
   } else {
-    G = num_cus / pl.U;
+    G = pl.U > kManyRows ? (kDynamicWaves * num_cus + pl.U - 1) / pl.U : num_cus / pl.U;
     if (G < 1) G = 1;
     long long cap = (units_max + kMinUnitsPerSlice - 1) / kMinUnitsPerSlice;
     if (cap < 1) cap = 1;
@@ -90,6 +98,7 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int num_cus, const mla_
   }
   pl.G = G;
   pl.xcd_map = (pl.U == 1 || G % 8 == 0) ? 1 : 0;
+  pl.u_major = pl.U > kManyRows ? 1 : 0;
   pl.rows_per_b = (size_t)q_len * H;
   if (G <= 1) {
     pl.bytes = 0;
@@ -100,7 +109,8 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int num_cus, const mla_
     pl.off_part_o = 0;
     pl.off_part_lse = align_up(slots * pl.rows_per_b * mla::kDv * esz);
     pl.off_meta = pl.off_part_lse + align_up(slots * pl.rows_per_b * sizeof(float));
-    pl.bytes = pl.off_meta + align_up((size_t)B * 2 * sizeof(int32_t) + sizeof(int64_t));  // + total units T
+    // per workgroup row: [B][2] slice ranges, then the rows' total units T
+    pl.bytes = pl.off_meta + align_up((size_t)pl.U * B * 2 * sizeof(int32_t) + (size_t)pl.U * sizeof(int64_t));
   }
   return pl;
 }
@@ -238,6 +248,7 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
   p.U = pl.U;
   p.G = pl.G;
   p.xcd_map = pl.xcd_map;
+  p.u_major = pl.u_major;
   p.page_size = s->page_size;
   p.page_shift = shift;
   p.max_pages = s->max_pages;
@@ -273,6 +284,9 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
     c.part_bf16 = pl.part_bf16;
     c.H = s->num_heads;
     c.q_len = s->q_len;
+    c.F = pl.F;
+    c.q_len_eff = pl.q_len_eff;
+    c.U = pl.U;
     c.cu_q = cu_q;
     c.total_q = total_q;
     e = mla::launch_combine(c, st);

@@ -33,9 +33,10 @@ struct PartialParams {
   float* lse;                // [B, q_len, H] or nullptr
   void* part_o;              // [G + B][q_len * H][512] fp32 or bf16
   float* part_lse;           // [G + B][q_len * H]
-  int32_t* meta;             // [B][2]: first and last KV slice touching sequence b; then int64 T
+  int32_t* meta;             // [U][B][2]: first and last KV slice of workgroup row u touching sequence b; then int64 T[U]
   int32_t B, q_len, H, F, H_eff, q_len_eff, m_tiles, U, G;
-  int32_t xcd_map;           // 1: the U workgroups of a slice are placed on one XCD
+  int32_t xcd_map;           // 1: slices are dealt to the XCDs in turn, each slice's workgroups on one XCD
+  int32_t u_major;           // 1: workgroup ids run over the slices of one query group first (many groups)
   int32_t page_size, page_shift, max_pages, num_pages;
   float s_scale_log2;        // softmax_scale * q_scale * kv_scale * log2(e)
   float v_scale;             // kv_scale (V dequantisation)
@@ -54,6 +55,7 @@ struct CombineParams {
   int32_t B, rows_per_b, G;
   int32_t part_bf16;
   int32_t H, q_len;           // heads and the (largest) query count of a sequence
+  int32_t F, q_len_eff, U;    // fold factor, query groups, workgroup rows (meta is [U][B][2], then int64 T[U])
   const int32_t* cu_q;        // ragged batch: [B+1] cumulative new-token counts, or nullptr
   int32_t total_q;
 };

@@ -221,17 +221,13 @@ template <int UK>
 __device__ __forceinline__ int units_of(int L) { return L > 0 ? (L + UK - 1) / UK : 1; }
 // First key any query token of a sequence of length L can see, rounded down
 // to a unit: 0 without a sliding window, else the earliest window start
-// (token 0's, n_0 - window) rounded down.  The sequence's work is the units
-// from there to L; tiles before it are never read.
+// (token 0's, n_0 - window) rounded down.  A query group's work is the units
+// from there to the last key it sees; tiles before it are never read.
 template <int UK>
 __device__ __forceinline__ int seq_key0(int L, int q_len, int window) {
   if (window <= 0) return 0;
   const long long lo = (long long)L - q_len + 1 - window;
   return lo > 0 ? (int)(lo & ~(long long)(UK - 1)) : 0;
-}
-template <int UK>
-__device__ __forceinline__ int seq_units(int L, int q_len, int window) {
-  return units_of<UK>(L - seq_key0<UK>(L, q_len, window));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -315,9 +311,9 @@ __device__ __forceinline__ void store_out(const v4i& v, v4i* dst, bool final_out
 }
 
 // ---------------------------------------------------------------------------
-// Balanced partition of the batch's KV work: sequence b owns seq_units(L_b)
-// consecutive units (one LDS tile each); slice w of G covers units
-// [w*T/G, (w+1)*T/G).
+// Balanced partition of one workgroup row's KV work (a query group g, one row
+// tile): sequence b owns group_units(b, g) consecutive units (one LDS tile
+// each); slice w of G covers units [w*T/G, (w+1)*T/G) of the row's total T.
 // Every (slice, sequence) intersection is one segment; its partial lives in
 // workspace slot w + b (unique along the monotone staircase of segments).
 // ---------------------------------------------------------------------------
@@ -358,12 +354,19 @@ __device__ __forceinline__ void seq_tokens(const PartialParams& p, int b, int& q
   }
 }
 
-// The query count seq_units needs: only a sliding window makes a sequence's units depend on it.
-__device__ __forceinline__ int units_qlen(const PartialParams& p, int b, int window) {
-  if (window <= 0) return p.q_len;
+// Units of query group g of sequence b: from the sequence's first unit to the
+// last key the group's last token sees.  A group holding no token of the
+// sequence (a ragged batch's shorter sequences) keeps one empty unit, so every
+// (group, sequence) pair has at least one.
+template <int UK>
+__device__ __forceinline__ int group_units(const PartialParams& p, int b, int g, int window) {
   int qlen_b, tok0;
   seq_tokens(p, b, qlen_b, tok0);
-  return qlen_b;
+  const int gF = g * p.F;
+  if (qlen_b <= gF) return 1;
+  const int L = max(((cint_t*)p.seq_lens)[b], 0);
+  const int n_gmax = min(max(L - qlen_b + gF + p.F, 0), L);
+  return units_of<UK>(n_gmax - seq_key0<UK>(L, qlen_b, window));
 }
 
 // XPV (16-bit paths): the fp8 path's cross-wave PV layout instead of the own-rows one.
@@ -1439,34 +1442,47 @@ mla_split_kv_partial(PartialParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases in SGPRs
   int w, u;
   if (p.xcd_map) {
-    // the U workgroups of one slice are consecutive dispatches of one XCD
+    // slices are dealt to the 8 XCDs in turn.  Few rows: the U workgroups of one
+    // slice are consecutive dispatches of one XCD (they read the same keys).
+    // Many rows: the G slices of one row are dispatched together, row by row.
     const int bid = blockIdx.x, xcd = bid & 7, idx = bid >> 3;
-    const int sl = idx / p.U;
-    u = idx - sl * p.U;
+    int sl;
+    if (p.u_major) {
+      const int gx = p.G >> 3;  // slices per XCD
+      u = idx / gx;
+      sl = idx - u * gx;
+    } else {
+      sl = idx / p.U;
+      u = idx - sl * p.U;
+    }
     w = sl * 8 + xcd;
+  } else if (p.u_major) {
+    u = blockIdx.x / p.G;
+    w = blockIdx.x - u * p.G;
   } else {
     w = blockIdx.x / p.U;
     u = blockIdx.x - w * p.U;
   }
+  if (u >= p.U) return;
   if (w >= p.G) return;
   const int g = u % p.q_len_eff;
   const int mt = u / p.q_len_eff;
 
-  // ---- total work T (units) and the slice's first sequence ----
+  // ---- total work T (units) of this row and the slice's first sequence ----
   // Every wave computes the same answer on its own (no LDS, no barrier): lane
   // i sums the units of sequences [i*kper, (i+1)*kper), one wave-wide prefix
   // sum gives T and each lane's first unit, and the lane whose range holds the
   // slice's first unit is found by ballot.
-  cint_t* seq_lens = (cint_t*)p.seq_lens;
   const int kper = (p.B + 63) >> 6;
   const int bl0 = min(lane * kper, p.B), bl1 = min(bl0 + kper, p.B);
   long long own = 0;
   const int window = WIN ? p.window : 0;
-  for (int bb = bl0; bb < bl1; ++bb) own += seq_units<UK>(p.seq_lens[bb], units_qlen(p, bb, window), window);
+  for (int bb = bl0; bb < bl1; ++bb) own += group_units<UK>(p, bb, g, window);
   const long long incl = wave_incl_scan_ll(own);
   const long long T = readlane_ll(incl, 63);
   // the merge needs T to recognise empty slices (they write no partials)
-  if (blockIdx.x == 0 && tid == 0 && p.meta != nullptr) *(long long*)(p.meta + 2 * p.B) = T;
+  int32_t* meta_u = p.meta != nullptr ? p.meta + 2 * (size_t)u * p.B : nullptr;
+  if (w == 0 && tid == 0 && meta_u != nullptr) ((long long*)(p.meta + 2 * (size_t)p.U * p.B))[u] = T;
   const long long t0 = slice_start(w, T, p.G), t1 = slice_start(w + 1, T, p.G);
   if (t0 >= t1) return;
   const long long excl = incl - own;
@@ -1476,7 +1492,7 @@ mla_split_kv_partial(PartialParams p) {
   long long P = readlane_ll(excl, hl);
   int b = hl * kper;
   while (b + 1 < p.B) {
-    const int nb = seq_units<UK>(seq_lens[b], units_qlen(p, b, window), window);
+    const int nb = group_units<UK>(p, b, g, window);
     if (t0 < P + nb) break;
     P += nb;
     ++b;
@@ -1485,7 +1501,7 @@ mla_split_kv_partial(PartialParams p) {
   // ---- segments of this slice ----
   long long cur = t0;
   while (cur < t1 && b < p.B) {
-    const int nb = seq_units<UK>(seq_lens[b], units_qlen(p, b, window), window);
+    const int nb = group_units<UK>(p, b, g, window);
     const long long seg_end = min(t1, P + nb);
     SegmentCtx sg;
     sg.b = b;
@@ -1493,9 +1509,9 @@ mla_split_kv_partial(PartialParams p) {
     sg.u1 = (int)(seg_end - P);
     sg.single = (sg.u0 == 0 && sg.u1 == nb);
     sg.slot = w + b;
-    if (p.meta != nullptr && sg.u0 == 0 && u == 0 && tid == 0) {
-      p.meta[2 * b] = w;
-      p.meta[2 * b + 1] = slice_of_unit(P + nb - 1, T, p.G);
+    if (meta_u != nullptr && sg.u0 == 0 && tid == 0) {
+      meta_u[2 * b] = w;
+      meta_u[2 * b + 1] = slice_of_unit(P + nb - 1, T, p.G);
     }
     run_segment<DT, FAST, WIN, XPV>(p, smem, s_flag, sg, g, mt, wave, lane);
     cur = seg_end;
@@ -1520,6 +1536,20 @@ __device__ __forceinline__ bool merge_out_row(const CombineParams& p, int b, int
   return true;
 }
 
+// The slices [w0, w1] holding partials of row `row` of sequence b, and the
+// total units T of the partition they come from: that of the workgroup row
+// (query group, row tile) the row belongs to.
+__device__ __forceinline__ void merge_slices(const CombineParams& p, int b, int row, int& w0, int& w1,
+                                             long long& T) {
+  const int t = row / p.H, h = row - t * p.H;
+  const int g = t / p.F, f = t - g * p.F;
+  const int u = ((f * p.H + h) / kTileM) * p.q_len_eff + g;
+  const int32_t* m = p.meta + 2 * ((size_t)u * p.B + b);
+  w0 = max(m[0], 0);
+  w1 = min(m[1], p.G - 1);
+  T = ((const long long*)(p.meta + 2 * (size_t)p.U * p.B))[u];
+}
+
 // ---------------------------------------------------------------------------
 // Merge: one workgroup per output row.  The slice weights exp(lse_s - LSE)
 // are computed once per row into LDS (256 slices at a time); each of the four
@@ -1536,12 +1566,13 @@ __global__ void __launch_bounds__(256) mla_combine(CombineParams p) {
   const int row = (int)(grow - (long long)b * p.rows_per_b);
   size_t orow;
   if (!merge_out_row(p, b, row, orow)) return;
-  const int w0 = max(p.meta[2 * b], 0), w1 = min(p.meta[2 * b + 1], p.G - 1);
+  int w0, w1;
+  long long T;
+  merge_slices(p, b, row, w0, w1, T);
   if (w0 >= w1) return;  // single slice: written by the partial kernel
   // slices that hold no work (more slices than units) wrote nothing: weight 0
-  const long long T = *(const long long*)(p.meta + 2 * p.B);
   auto lse_of = [&](int s) -> float {
-    if (slice_start(s, T, p.G) == slice_start(s + 1, T, p.G)) return -INFINITY;
+    if (T < p.G && slice_start(s, T, p.G) == slice_start(s + 1, T, p.G)) return -INFINITY;
     return p.part_lse[(size_t)(s + b) * p.rows_per_b + row];
   };
   const int n = w1 - w0 + 1;
@@ -1615,18 +1646,20 @@ __global__ void __launch_bounds__(256) mla_combine(CombineParams p) {
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) mla_combine_rows(CombineParams p) {
   const int lane = threadIdx.x & 63;
-  const long long grow = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform: the row, its slice range and T are then scalar values
+  const long long grow = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (grow >= (long long)p.B * p.rows_per_b) return;
   const int b = (int)(grow / p.rows_per_b);
   const int row = (int)(grow - (long long)b * p.rows_per_b);
   size_t orow;
   if (!merge_out_row(p, b, row, orow)) return;
-  const int w0 = max(p.meta[2 * b], 0), w1 = min(p.meta[2 * b + 1], p.G - 1);
+  int w0, w1;
+  long long T;
+  merge_slices(p, b, row, w0, w1, T);
   if (w0 >= w1) return;  // single slice: written by the partial kernel
   const int n = w1 - w0 + 1;
-  const long long T = *(const long long*)(p.meta + 2 * p.B);
   auto lse_of = [&](int s) -> float {
-    if (slice_start(s, T, p.G) == slice_start(s + 1, T, p.G)) return -INFINITY;
+    if (T < p.G && slice_start(s, T, p.G) == slice_start(s + 1, T, p.G)) return -INFINITY;
     return p.part_lse[(size_t)(s + b) * p.rows_per_b + row];
   };
   float mx = -INFINITY;

@@ -527,7 +527,8 @@ def test_lengths_above_the_planned_maximum():
 
 # ---------------------------------------------------------------- many new tokens per sequence (prefill-sized q_len)
 @pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
-@pytest.mark.parametrize("B,q_len,H,lens", [(2, 96, 16, [700, 300]), (1, 256, 8, [1024]), (2, 60, 32, [60, 2000])])
+@pytest.mark.parametrize("B,q_len,H,lens", [(2, 96, 16, [700, 300]), (1, 256, 8, [1024]), (2, 60, 32, [60, 2000]),
+                                             (2, 264, 16, [300, 264])])  # 33 workgroup rows: the many-rows plan
 def test_prefill_sized_query_counts(dtype, B, q_len, H, lens):
     """q_len in the hundreds: the causal mask runs across the new tokens, folded groups stream
     only the keys they can see (sequences as long as q_len see no cached prefix at all)."""
@@ -569,6 +570,10 @@ RAGGED_CASES = [
     (mi.BF16_Q_E4M3_KV, 16, [12, 5, 1], [900, 5, 3000], {"num_splits": 40}),
     (mi.FP16, 128, [2, 9, 1], [1500, 300, 64], {}),
     (mi.FP8_E4M3, 64, [6, 2, 5, 1, 6], [700, 1, 1300, 64, 6], {"partial_fp32": True}),
+    # many workgroup rows (query groups x row tiles > 32): a partition per row, ~4 workgroups per CU
+    (mi.FP8_E4M3, 16, [300, 8, 129], [1200, 8, 500], {}),                 # F = 6, 50 rows, G = 16
+    (mi.BF16, 8, [150, 0, 37, 150], [400, 5, 90, 150], {"no_fold": True}),  # 150 rows, G = 7
+    (mi.FP8_E4M3, 16, [64, 200], [3000, 300], {"no_fold": True, "num_splits": 5}),
 ]
 
 
