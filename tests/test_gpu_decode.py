@@ -570,9 +570,9 @@ RAGGED_CASES = [
     (mi.BF16_Q_E4M3_KV, 16, [12, 5, 1], [900, 5, 3000], {"num_splits": 40}),
     (mi.FP16, 128, [2, 9, 1], [1500, 300, 64], {}),
     (mi.FP8_E4M3, 64, [6, 2, 5, 1, 6], [700, 1, 1300, 64, 6], {"partial_fp32": True}),
-    # many workgroup rows (query groups x row tiles > 32): a partition per row, ~4 workgroups per CU
-    (mi.FP8_E4M3, 16, [300, 8, 129], [1200, 8, 500], {}),                 # F = 6, 50 rows, G = 16
-    (mi.BF16, 8, [150, 0, 37, 150], [400, 5, 90, 150], {"no_fold": True}),  # 150 rows, G = 7
+    # many workgroup rows (query groups x row tiles > 32): a partition per row, ~2 workgroups per CU
+    (mi.FP8_E4M3, 16, [300, 8, 129], [1200, 8, 500], {}),                 # F = 6, 50 rows, G = 8
+    (mi.BF16, 8, [150, 0, 37, 150], [400, 5, 90, 150], {"no_fold": True}),  # 150 rows, G = 4
     (mi.FP8_E4M3, 16, [64, 200], [3000, 300], {"no_fold": True, "num_splits": 5}),
 ]
 
