@@ -8,6 +8,11 @@ inputs resident in HBM.  The default workload is B=4, q_len=4, H=32, FP8 E4M3,
 enough rotating copies that consecutive steps never find their cache in the
 256 MB Infinity Cache.
 
+Before the timed steps come the W warm-up steps and then as many more as it
+takes to keep the GPU busy for --warmup-ms (default 250 ms): from idle, its
+clocks take some 40 ms of sustained load to settle, and a serving GPU runs at
+the settled clocks.
+
 Prints one JSON line: metric / value (effective KV-read TB/s) / ms_per_step,
 the roofline of the dominant kernel measured live with HIP events on the
 launch stream, and the fp64 CPU oracle timed on a bounded sample of the same
@@ -91,6 +96,25 @@ def load_traffic(workload: str):
 COPY_BYTES = 256 << 20
 
 
+def warm_up(run_one, min_steps: int, min_ms: float) -> tuple[int, float]:
+    """Untimed steps: at least min_steps, and more until min_ms of wall time has passed with the GPU
+    kept busy (the host waits for the GPU every 16 steps).  Returns (steps run, ms)."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(min_steps):
+        run_one(n)
+        n += 1
+    torch.cuda.synchronize()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(16):
+            run_one(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n, (time.perf_counter() - t0) * 1e3
+
+
 def copy_calibration():
     """A plain device copy of known size, for scaling the rocprofv3 byte counters.
 
@@ -129,9 +153,11 @@ def _counter_avg(path, counter, name_part):
     return sum(vals) / len(vals), len(vals)
 
 
-def _trace_regions(path):
+def _trace_regions(path, steps=50):
     """Per-region kernel timings from the dispatch trace of one bench.py run, in the order bench.py runs
-    them: steps (split-KV then merge), split-KV alone back to back, merge alone back to back."""
+    them: steps (split-KV then merge), split-KV alone back to back, merge alone back to back.  Each
+    region is averaged over its last `steps` launches, the timed ones: the warm-up steps run just
+    before the timed steps, in the same pattern."""
     import csv
     import glob
     import re
@@ -151,19 +177,19 @@ def _trace_regions(path):
         per = [(ev[j][0] - ev[i][0]) / 1e3 for i, j in zip(idx[:-1], idx[1:])]
         return round(sum(dur) / len(dur), 2), round(sum(per) / len(per), 2) if per else None
 
-    m = re.search(r"(?:PM){5,}", seq)  # the timed steps (the first run of them)
+    m = re.search(r"(?:PM){5,}", seq)  # the warm-up and timed steps (the first run of them)
     if m:
-        ps = list(range(m.start(), m.end(), 2))
+        ps = list(range(m.start(), m.end(), 2))[-steps:]
         d_p, period = stats(ps, 2)
         d_m, _ = stats([i + 1 for i in ps], 2)
         out["steps"] = {"split_kv_us": d_p, "merge_us": d_m, "step_period_us": period}
     m = re.search(r"P{5,}", seq)
     if m:
-        d_p, period = stats(list(range(m.start(), m.end())), 1)
+        d_p, period = stats(list(range(m.start(), m.end()))[-steps:], 1)
         out["split_kv_alone"] = {"duration_us": d_p, "period_us": period}
     m = re.search(r"M{5,}", seq)
     if m:
-        d_m, period = stats(list(range(m.start(), m.end())), 1)
+        d_m, period = stats(list(range(m.start(), m.end()))[-steps:], 1)
         out["merge_alone"] = {"duration_us": d_m, "period_us": period}
     return out
 
@@ -194,9 +220,11 @@ def summarize_profile(d: str, workload: str):
     base = os.path.join(ROOT, "profiles")
     with open(os.path.join(base, f"mla_split_kv_partial_{workload}_traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
+    ran = ("the warm-up and timed steps of `mla_decode_varlen`, then the split-KV kernel alone"
+           if workload.startswith("ragged_prefill") else
+           "the warm-up, the timed steps, each kernel alone, and two replays of the captured graph")
     lines = [f"# rocprofv3 summary: {workload}", "",
-             "Kernel trace (`--kernel-trace --stats`) of one `bench.py --steps 50 --warmup 50` run: the warm-up, the "
-             "timed steps, each kernel alone, and two replays of the captured graph:", "",
+             f"Kernel trace (`--kernel-trace --stats`) of one `bench.py --steps 50 --warmup 50` run: {ran}:", "",
              "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
     for r in stats:
         lines.append(f"| {r['Name'][:70]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
@@ -207,7 +235,7 @@ def summarize_profile(d: str, workload: str):
                   "start-to-start, so they include the dispatch gaps bench.py's events also see):", ""]
         if "steps" in reg:
             r = reg["steps"]
-            lines.append(f"- steps: split-KV {r['split_kv_us']} us, merge {r['merge_us']} us, one step every "
+            lines.append(f"- timed steps: split-KV {r['split_kv_us']} us, merge {r['merge_us']} us, one step every "
                          f"{r['step_period_us']} us")
         if "split_kv_alone" in reg:
             r = reg["split_kv_alone"]
@@ -280,9 +308,7 @@ def bench_pack(args):
     def run():
         mla.kv_pack_quantize_fp8(latent, rope, kv_scale, slot_mapping=slots, out=out)
 
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
+    warm_up(lambda i: run(), args.warmup, args.warmup_ms)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
@@ -331,13 +357,13 @@ def bench_ragged(args):
     G, ws_bytes = mla.plan(B, max_new, H, x.max_seq_len)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
+    warm = {}
+
     def timed(stages):
         opts = mla.options(stages=stages)
         run = lambda: mla.decode_varlen(q, cu, kv, bt, sl, x.softmax_scale, x.q_scale, x.kv_scale, max_q_len=max_new,
                                         max_seq_len=x.max_seq_len, out=out, lse=lse, workspace=ws, opts=opts)
-        for _ in range(args.warmup):
-            run()
-        torch.cuda.synchronize()
+        warm[stages] = warm_up(lambda i: run(), args.warmup, args.warmup_ms)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.steps):
@@ -356,13 +382,15 @@ def bench_ragged(args):
     tfs = flops / (part * 1e-3) / 1e12
     print(json.dumps({"metric": "ragged prefill over the paged latent cache (mla_decode_varlen)",
                       "value": round(flops / (ms * 1e-3) / 1e12, 1), "unit": "TFLOP/s", "n_gpus": 1,
-                      "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+                      "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": warm[0][0],
+                      "warmup_ms": round(warm[0][1], 1), "ms_per_step": round(ms, 5),
                       "us_per_step": round(ms * 1e3, 2), "higher_is_better": True, "dtype": DTYPE_NAMES[dtype],
                       "data": "synthetic",
                       "config": {"workload": args.workload, "new_tokens": new, "cached_keys": ctx, "num_heads": H,
                                  "num_splits": G, "page_size": 64},
                       "roofline": {"bound": "mfma", "kernel": "mla_split_kv_partial", "achieved": round(tfs, 1),
                                    "peak": peak, "unit": "TFLOP/s", "frac": round(tfs / peak, 4),
+                                   "traffic": load_traffic(args.workload),
                                    "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,
                                    "avg_launch_ms": round(part, 5)},
                       "kernels_ms": {"split_kv_partial": round(part, 5)}}), flush=True)
@@ -373,6 +401,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup-ms", type=float, default=250.0,
+                    help="keep warming up until this much wall time has passed (the GPU's clocks settle)")
     ap.add_argument("--workload", default="agentic_b4_q4_h32_fp8_80k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=16)
@@ -390,8 +420,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "sequences are independent, see DESIGN.md for how the decode would shard", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
+              "sequences are independent, so the decode would shard by batch, each GPU with its own sequences and cache", file=sys.stderr)
         sys.exit(2)
     if args.pack_tokens > 0:
         bench_pack(args)
@@ -486,20 +516,18 @@ def main():
         return e0.elapsed_time(e1) / K, time.perf_counter() - t0
 
     prepare(0)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    n_warm, warm_ms = warm_up(step, args.warmup, args.warmup_ms)
 
     K = args.steps
     # the step: both kernels, K times back to back (the headline figure)
     t0 = time.perf_counter()
-    ms_per_step = timed_eager(0, args.warmup)
+    ms_per_step = timed_eager(0, n_warm)
     wall = time.perf_counter() - t0
     # each kernel alone, back to back, for its roofline (the merge re-merges the partials just written)
-    part_avg = timed_eager(1, args.warmup + K)
-    merge_avg = timed_eager(2, args.warmup + 2 * K) if num_splits > 1 else 0.0
+    part_avg = timed_eager(1, n_warm + K)
+    merge_avg = timed_eager(2, n_warm + 2 * K) if num_splits > 1 else 0.0
     # the same K steps captured into one HIP graph and replayed (reported beside the headline)
-    graph_ms, _ = timed_graph(0, args.warmup)
+    graph_ms, _ = timed_graph(0, n_warm)
 
     value = alg["kv_bytes"] / (ms_per_step * 1e-3) / 1e12
     # the split-KV kernel against the roofline that binds it: HBM bytes at 8 TB/s or MFMA flops at
@@ -518,6 +546,8 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "warmup_steps_run": n_warm,
+        "warmup_ms": round(warm_ms, 1),
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
         "graph_us_per_step": round(graph_ms * 1e3, 2),
