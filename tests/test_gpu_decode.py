@@ -528,7 +528,8 @@ def test_lengths_above_the_planned_maximum():
 # ---------------------------------------------------------------- many new tokens per sequence (prefill-sized q_len)
 @pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
 @pytest.mark.parametrize("B,q_len,H,lens", [(2, 96, 16, [700, 300]), (1, 256, 8, [1024]), (2, 60, 32, [60, 2000]),
-                                             (2, 264, 16, [300, 264])])  # 33 workgroup rows: the many-rows plan
+                                             (2, 264, 16, [300, 264]),  # 33 workgroup rows: the many-rows plan
+                                             (2, 20, 256, [150, 300])])  # 20 groups x 2 row tiles = 40 rows
 def test_prefill_sized_query_counts(dtype, B, q_len, H, lens):
     """q_len in the hundreds: the causal mask runs across the new tokens, folded groups stream
     only the keys they can see (sequences as long as q_len see no cached prefix at all)."""
