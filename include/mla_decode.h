@@ -92,9 +92,10 @@ typedef struct mla_shape {
  * max_seq_len) and the current device's compute-unit count and cached per
  * shape, so callers never tune them (article, section 2: split_kv and the
  * workspace size are derived at run time from batch size, q_len and
- * max_seq_len, and cached).  num_splits is the number of KV slices the
- * batch's total work is cut into; workspace_bytes is what mla_decode needs
- * for that shape (0 when no merge is needed).
+ * max_seq_len, and cached).  num_splits is the number of KV slices that
+ * each workgroup row's work (one query group of F folded tokens and up to 128
+ * of its rows, over every sequence of the batch) is cut into; workspace_bytes
+ * is what mla_decode needs for that shape (0 when no merge is needed).
  *
  * Inputs are host integers; outputs are host pointers (must be non-NULL).
  * Errors: MLA_ERR_NULL, MLA_ERR_SHAPE (batch < 0, q_len < 1, num_heads < 1,
