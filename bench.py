@@ -167,7 +167,7 @@ def _trace_regions(path, steps=50):
         return {}
     with open(files[0]) as f:
         ev = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
-                     "P" if "split_kv_partial" in r["Kernel_Name"] else "M" if "combine" in r["Kernel_Name"] else "o")
+                     "P" if "mla_split_kv" in r["Kernel_Name"] else "M" if "combine" in r["Kernel_Name"] else "o")
                     for r in csv.DictReader(f))
     seq = "".join(e[2] for e in ev)
     out = {}
@@ -206,7 +206,7 @@ def summarize_profile(d: str, workload: str):
            "calibration": {"copy_bytes": COPY_BYTES, "fetch_kib": cal_f, "write_kib": cal_w,
                            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
            "kernels": {}}
-    for short, part in (("mla_split_kv_partial", "mla_split_kv_partial"), ("mla_combine", "mla_combine")):
+    for short, part in (("mla_split_kv_partial", "mla_split_kv"), ("mla_combine", "mla_combine")):
         fk, nf = _counter_avg(os.path.join(d, "fetch"), "FETCH_SIZE", part)
         wk, nw = _counter_avg(os.path.join(d, "write"), "WRITE_SIZE", part)
         st = [r for r in stats if part in r["Name"]]
@@ -408,6 +408,9 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--num-splits", type=int, default=0, help="override the planned KV slice count")
     ap.add_argument("--partial-fp32", action="store_true", help="keep split partials in fp32 (default bf16)")
+    ap.add_argument("--kernel", type=int, default=0,
+                    help="E4M3 split-KV kernel: 0 default, 1 four-wave, 2 twelve-wave role-specialised")
+    ap.add_argument("--merge", type=int, default=0, help="merge kernel: 0 wide (default), 1 workgroup per row")
     ap.add_argument("--copy-calibration", action="store_true", help="run the counter-calibration copy and exit")
     ap.add_argument("--summarize-profile", metavar="DIR", help="summarise rocprofv3 runs under DIR into profiles/")
     ap.add_argument("--pack-tokens", type=int, default=0,
@@ -456,7 +459,8 @@ def main():
     B, q_len, H = x.B, x.q_len, x.H
     out = torch.empty(B, q_len, H, 512, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(B, q_len, H, dtype=torch.float32, device=dev)
-    base_opts = mla.options(num_splits=args.num_splits, partial_fp32=args.partial_fp32)
+    base_opts = mla.options(num_splits=args.num_splits, partial_fp32=args.partial_fp32, kernel=args.kernel,
+                            merge=args.merge)
     num_splits, ws_bytes = mla.plan(B, q_len, H, x.max_seq_len, base_opts)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -469,7 +473,8 @@ def main():
         stream) so the loop measures the kernels, not the Python binding."""
         key = (i % copies, stages, (st or stream).cuda_stream)
         if key not in calls:
-            opts = mla.options(num_splits=args.num_splits, partial_fp32=args.partial_fp32, stages=stages)
+            opts = mla.options(num_splits=args.num_splits, partial_fp32=args.partial_fp32, stages=stages,
+                               kernel=args.kernel, merge=args.merge)
             calls[key] = mla.PreparedDecode(q, kvs[i % copies], bt, sl, x.softmax_scale, x.q_scale, x.kv_scale,
                                             max_seq_len=x.max_seq_len, out=out, lse=lse, workspace=ws, opts=opts,
                                             stream=(st or stream).cuda_stream)

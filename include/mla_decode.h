@@ -61,7 +61,8 @@ typedef enum mla_status {
   MLA_ERR_WORKSPACE = -5,   /* workspace NULL, too small, misaligned, or planned for another shape */
   MLA_ERR_UNSUPPORTED = -6, /* valid but not implemented */
   MLA_ERR_HIP = -7,         /* a HIP runtime call failed (message names it) */
-  MLA_ERR_DEVICE = -8       /* no usable HIP device */
+  MLA_ERR_DEVICE = -8,      /* no usable HIP device */
+  MLA_ERR_STRIDE = -9       /* a tensor descriptor's strides are not the layout the kernels read */
 } mla_status;
 
 typedef enum mla_dtype {
@@ -147,7 +148,8 @@ int mla_decode(const mla_shape* shape, const void* q, const void* kv_cache, cons
 typedef struct mla_options {
   int32_t num_splits;   /* > 0: use this many KV slices instead of the planned count */
   int32_t no_fold;      /* != 0: do not fold query tokens into heads (F = 1) */
-  int32_t partial_fp32; /* != 0: keep the split partial outputs in fp32 (default: bf16) */
+  int32_t partial_fp32; /* != 0: keep the split partial outputs in fp32 (default: bf16 for E4M3
+                           caches, fp32 for bf16 / fp16 caches) */
   int32_t stages;       /* 0: both kernels; 1: only the split-KV kernel; 2: only the merge kernel
                            (re-merging the partials a previous call with the same arguments left in
                            the workspace).  1 and 2 exist to time each kernel back to back. */
@@ -158,7 +160,13 @@ typedef struct mla_options {
                            MLA article, section 6: a sliding-window mask among the decode
                            tests; the convention is this library's reading.)  < 0:
                            MLA_ERR_SHAPE.  Plan the workspace with the same options. */
-  int32_t reserved[3];
+  int32_t kernel;       /* E4M3 inputs: 1 the four-wave split-KV kernel, 2 the twelve-wave
+                           role-specialised one (the default, 0); other dtypes ignore it.
+                           Other values: MLA_ERR_SHAPE */
+  int32_t merge;        /* rows merged from many slices: 0 the wide merge (a wave per quarter row,
+                           a whole chunk of slices in flight; the default), 1 a workgroup per row
+                           (kept for comparison).  Other values: MLA_ERR_SHAPE */
+  int32_t reserved[1];
   void* split_event;    /* hipEvent_t or NULL: recorded on `stream` after the split-KV kernel
                            and before the merge kernel, so callers can time each kernel */
 } mla_options;
@@ -199,6 +207,64 @@ int mla_decode_varlen(const mla_shape* shape, const void* q, const int32_t* cu_s
                       const void* kv_cache, const int32_t* block_table, const int32_t* seq_lens, float softmax_scale,
                       float q_scale, float kv_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
                       void* stream, const mla_options* options);
+
+/*
+ * Tensor-descriptor form of mla_decode_ex, for C callers that hold strided
+ * views: every tensor carries its element type, shape and strides, and the
+ * library checks them against the layouts the kernels read before anything
+ * is enqueued.  The operation, ownership, stream and error conventions are
+ * those of mla_decode (top of this file); the argument list is the decode
+ * call of the TokenSpeed MLA article, section 6 (query, kv_cache,
+ * block_tables, cache_seqlens, softmax_scale, output / LSE, workspace).
+ *
+ * mla_tensor: data is a device pointer; dtype an mla_elem; ndim the number of
+ * dimensions used (<= 4); shape and stride (in elements, as torch reports
+ * them) of each dimension.  A dimension of extent 1 may have any stride.
+ *
+ *   q           ndim 4, [batch, q_len, num_heads, 576], bf16 / fp16 / E4M3, contiguous.
+ *   kv_cache    ndim 3, [num_pages, page_size, 576], contiguous; its element type with
+ *               q's selects the mla_dtype (equal, or bf16 q over an E4M3 cache).
+ *   block_table ndim 2, int32 [batch, max_pages], packed rows (stride {max_pages, 1}).
+ *   seq_lens    ndim 1, int32 [batch], unit stride.
+ *   out         ndim 4, bf16 [batch, q_len, num_heads, 512], contiguous.
+ *   lse         NULL, or ndim 3, fp32 [batch, q_len, num_heads], contiguous.
+ *   workspace   host descriptor (required): data / bytes as mla_decode's workspace,
+ *               max_seq_len the bound the plan was made for (0 <= max_seq_len <=
+ *               max_pages * page_size), num_splits the plan's split count or 0 (not
+ *               checked); a non-zero value other than the plan's is MLA_ERR_WORKSPACE.
+ *   options     as mla_decode_ex (NULL = defaults).
+ *
+ * Errors: MLA_ERR_NULL (a NULL descriptor or data pointer), MLA_ERR_DTYPE (element types),
+ * MLA_ERR_SHAPE (ndim, extents that disagree between tensors), MLA_ERR_STRIDE (strides),
+ * then every error of mla_decode_ex.
+ */
+typedef enum mla_elem {
+  MLA_ELEM_BF16 = 1,
+  MLA_ELEM_FP8_E4M3 = 2,
+  MLA_ELEM_FP16 = 3,
+  MLA_ELEM_FP32 = 4,
+  MLA_ELEM_INT32 = 5
+} mla_elem;
+
+typedef struct mla_tensor {
+  void* data;
+  int32_t dtype; /* mla_elem */
+  int32_t ndim;
+  int64_t shape[4];
+  int64_t stride[4];
+} mla_tensor;
+
+typedef struct mla_workspace {
+  void* data;
+  size_t bytes;
+  int32_t num_splits;
+  int32_t max_seq_len;
+} mla_workspace;
+
+int mla_decode_tensors(const mla_tensor* q, const mla_tensor* kv_cache, const mla_tensor* block_table,
+                       const mla_tensor* seq_lens, float softmax_scale, float q_scale, float kv_scale,
+                       const mla_tensor* out, const mla_tensor* lse, const mla_workspace* workspace, void* stream,
+                       const mla_options* options);
 
 /* Workspace size and split count for mla_decode_ex with `options` (NULL = defaults). */
 int mla_workspace_bytes_ex(int32_t batch, int32_t q_len, int32_t num_heads, int32_t max_seq_len,

@@ -9,6 +9,8 @@ Entry points mirror include/mla_decode.h:
   plan(B, q_len, H, max_seq_len)            -> (num_splits, workspace_bytes)
   decode(q, kv_cache, block_table, seq_lens, softmax_scale, ...) -> (out, lse)
   decode_varlen(q, cu_seqlens_q, kv_cache, block_table, seq_lens, ...) -> (out, lse)
+  decode_tensors(q, kv_cache, block_table, seq_lens, ..., out=, workspace=) -> (out, lse)
+      (per-tensor descriptors: the library checks element types, extents and strides)
   kv_pack_quantize_fp8(latent, rope, kv_scale, ...) -> uint8 rows [T, 576]
 """
 from __future__ import annotations
@@ -27,11 +29,15 @@ DTYPE_FP16 = 3
 DTYPE_BF16_Q_FP8_KV = 4  # bf16 q over an E4M3 cache
 
 STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_DTYPE", -3: "MLA_ERR_SHAPE", -4: "MLA_ERR_ALIGN",
-          -5: "MLA_ERR_WORKSPACE", -6: "MLA_ERR_UNSUPPORTED", -7: "MLA_ERR_HIP", -8: "MLA_ERR_DEVICE"}
+          -5: "MLA_ERR_WORKSPACE", -6: "MLA_ERR_UNSUPPORTED", -7: "MLA_ERR_HIP", -8: "MLA_ERR_DEVICE",
+          -9: "MLA_ERR_STRIDE"}
+# mla_elem codes of the tensor descriptors
+ELEM_BF16, ELEM_FP8_E4M3, ELEM_FP16, ELEM_FP32, ELEM_INT32 = 1, 2, 3, 4, 5
 
 # every symbol include/mla_decode.h declares
 EXPORTS = ["mla_get_split_kv_and_workspace", "mla_decode", "mla_decode_ex", "mla_decode_varlen",
-           "mla_workspace_bytes_ex", "mla_plan_for_cus", "mla_kv_pack_quantize_fp8", "mla_last_error", "mla_version"]
+           "mla_decode_tensors", "mla_workspace_bytes_ex", "mla_plan_for_cus", "mla_kv_pack_quantize_fp8",
+           "mla_last_error", "mla_version"]
 
 
 class MlaError(RuntimeError):
@@ -48,21 +54,36 @@ class MlaShape(ctypes.Structure):
 
 class MlaOptions(ctypes.Structure):
     _fields_ = [("num_splits", ctypes.c_int32), ("no_fold", ctypes.c_int32), ("partial_fp32", ctypes.c_int32),
-                ("stages", ctypes.c_int32), ("window", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3),
+                ("stages", ctypes.c_int32), ("window", ctypes.c_int32), ("kernel", ctypes.c_int32),
+                ("merge", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1),
                 ("split_event", ctypes.c_void_p)]
 
 
+class MlaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class MlaWorkspace(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("bytes", ctypes.c_size_t), ("num_splits", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32)]
+
+
 def options(num_splits: int = 0, no_fold: bool = False, partial_fp32: bool = False, split_event=None,
-            stages: int = 0, window: int = 0) -> MlaOptions:
+            stages: int = 0, window: int = 0, kernel: int = 0, merge: int = 0) -> MlaOptions:
     """mla_options; split_event is a raw hipEvent_t (e.g. torch.cuda.Event().cuda_event after one record);
     stages 1 / 2 launch only the split-KV / only the merge kernel; window > 0 is the sliding-window mask
-    (token t sees keys [max(0, n_t - window), n_t))."""
+    (token t sees keys [max(0, n_t - window), n_t)); kernel 1 / 2 select the four-wave / the
+    role-specialised twelve-wave E4M3 split-KV kernel (0: the default, 2); merge 1 selects the
+    workgroup-per-row merge for rows spread over many slices (0: the wide merge)."""
     o = MlaOptions()
     o.num_splits = int(num_splits)
     o.no_fold = int(bool(no_fold))
     o.partial_fp32 = int(bool(partial_fp32))
     o.stages = int(stages)
     o.window = int(window)
+    o.kernel = int(kernel)
+    o.merge = int(merge)
     o.split_event = split_event
     return o
 
@@ -92,11 +113,15 @@ def lib():
                                     ctypes.POINTER(MlaOptions)]
     L.mla_kv_pack_quantize_fp8.argtypes = [p, ctypes.c_int64, p, ctypes.c_int64, p, i32, ctypes.c_float, p,
                                            ctypes.c_int64, p]
+    tp = ctypes.POINTER(MlaTensor)
+    L.mla_decode_tensors.argtypes = [tp, tp, tp, tp, fl, fl, fl, tp, tp, ctypes.POINTER(MlaWorkspace), p,
+                                     ctypes.POINTER(MlaOptions)]
     L.mla_last_error.restype = ctypes.c_char_p
     L.mla_last_error.argtypes = []
     L.mla_version.restype = ctypes.c_int
     for f in ("mla_get_split_kv_and_workspace", "mla_workspace_bytes_ex", "mla_plan_for_cus", "mla_decode",
-              "mla_decode_ex", "mla_decode_varlen", "mla_kv_pack_quantize_fp8"):
+              "mla_decode_ex", "mla_decode_varlen", "mla_decode_tensors",
+              "mla_kv_pack_quantize_fp8"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -166,7 +191,8 @@ def make_shape(q, kv_cache, block_table, max_seq_len: int) -> MlaShape:
     return s
 
 
-def _check_layout(q, kv_cache, block_table, seq_lens):
+def _check_layout(q, kv_cache, block_table, seq_lens, batch=None):
+    """Layouts the kernels read; `batch` is the number of sequences (q.shape[0] when None)."""
     torch = _torch()
     if q.dim() != 4 or q.shape[3] != D_QK or not q.is_contiguous():
         raise ValueError("q must be a contiguous [B, q_len, H, 576] tensor")
@@ -179,6 +205,32 @@ def _check_layout(q, kv_cache, block_table, seq_lens):
         raise ValueError("block_table rows must be packed (row stride = max_pages)")
     if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or not seq_lens.is_contiguous():
         raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
+    B = int(q.shape[0]) if batch is None else int(batch)
+    if block_table.shape[0] != B or seq_lens.numel() != B:
+        raise ValueError(f"block_table must have {B} rows and seq_lens {B} entries (one per sequence)")
+
+
+def _check_device(q, *others):
+    """Every tensor on q's HIP device (the library reads and writes them there)."""
+    if q.device.type != "cuda":
+        raise ValueError("q must be on a HIP device")
+    for name, t in others:
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device} (is on {t.device})")
+
+
+def _check_outputs(q, out, lse, workspace, out_shape, lse_shape):
+    """Caller-supplied out / lse / workspace: dtype, shape and layout the kernels write."""
+    torch = _torch()
+    if out is not None and (out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(out_shape)
+                            or not out.is_contiguous()):
+        raise ValueError(f"out must be a contiguous bfloat16 tensor of shape {tuple(out_shape)}")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != tuple(lse_shape)
+                            or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {tuple(lse_shape)}")
+    if workspace is not None and (workspace.dtype != torch.uint8 or workspace.dim() != 1
+                                  or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
 
 
 def decode(q, kv_cache, block_table, seq_lens, softmax_scale: float, q_scale: float = 1.0, kv_scale: float = 1.0,
@@ -194,10 +246,13 @@ def decode(q, kv_cache, block_table, seq_lens, softmax_scale: float, q_scale: fl
     """
     torch = _torch()
     _check_layout(q, kv_cache, block_table, seq_lens)
+    B, q_len, H = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    _check_outputs(q, out, lse, workspace, (B, q_len, H, D_V), (B, q_len, H))
+    _check_device(q, ("kv_cache", kv_cache), ("block_table", block_table), ("seq_lens", seq_lens), ("out", out),
+                  ("lse", lse), ("workspace", workspace))
     if max_seq_len is None:
         max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0
     shape = make_shape(q, kv_cache, block_table, max_seq_len)
-    B, q_len, H = shape.batch, shape.q_len, shape.num_heads
     if out is None:
         out = torch.empty((B, q_len, H, D_V), dtype=torch.bfloat16, device=q.device)
     if lse is None and return_lse:
@@ -231,10 +286,11 @@ def decode_varlen(q, cu_seqlens_q, kv_cache, block_table, seq_lens, softmax_scal
         raise ValueError("cu_seqlens_q must be a contiguous int32 [B + 1] tensor")
     B = int(cu_seqlens_q.numel()) - 1
     q4 = q.view(1, q.shape[0], q.shape[1], D_QK)  # layout checks only
-    _check_layout(q4, kv_cache, block_table, seq_lens)
-    if block_table.shape[0] != B or seq_lens.numel() != B:
-        raise ValueError("block_table and seq_lens must have one row / entry per sequence")
+    _check_layout(q4, kv_cache, block_table, seq_lens, batch=B)
     total_q, H = int(q.shape[0]), int(q.shape[1])
+    _check_outputs(q, out, lse, workspace, (total_q, H, D_V), (total_q, H))
+    _check_device(q, ("cu_seqlens_q", cu_seqlens_q), ("kv_cache", kv_cache), ("block_table", block_table),
+                  ("seq_lens", seq_lens), ("out", out), ("lse", lse), ("workspace", workspace))
     shape = make_shape(q4, kv_cache, block_table, max_seq_len)
     shape.batch, shape.q_len, shape.num_heads = B, int(max_q_len), H
     if out is None:
@@ -262,6 +318,10 @@ class PreparedDecode:
                  *, max_seq_len: int, out, lse, workspace, opts: MlaOptions | None = None, stream=None):
         torch = _torch()
         _check_layout(q, kv_cache, block_table, seq_lens)
+        B, q_len, H = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+        _check_outputs(q, out, lse, workspace, (B, q_len, H, D_V), (B, q_len, H))
+        _check_device(q, ("kv_cache", kv_cache), ("block_table", block_table), ("seq_lens", seq_lens),
+                      ("out", out), ("lse", lse), ("workspace", workspace))
         self._keep = (q, kv_cache, block_table, seq_lens, out, lse, workspace)
         self._shape = make_shape(q, kv_cache, block_table, max_seq_len)
         self._opts = opts if opts is not None else options()
@@ -280,6 +340,45 @@ class PreparedDecode:
             _check(rc)
 
 
+def tensor_desc(t) -> MlaTensor:
+    """mla_tensor of a torch tensor (device pointer, element type, shape and strides in elements)."""
+    torch = _torch()
+    elem = {torch.bfloat16: ELEM_BF16, torch.float8_e4m3fn: ELEM_FP8_E4M3, torch.uint8: ELEM_FP8_E4M3,
+            torch.float16: ELEM_FP16, torch.float32: ELEM_FP32, torch.int32: ELEM_INT32}
+    if t.dim() > 4:
+        raise ValueError("descriptors hold at most 4 dimensions")
+    d = MlaTensor()
+    d.data = t.data_ptr()
+    d.dtype = elem.get(t.dtype, 0)
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = int(t.shape[i])
+        d.stride[i] = int(t.stride(i))
+    return d
+
+
+def decode_tensors(q, kv_cache, block_table, seq_lens, softmax_scale: float, q_scale: float = 1.0,
+                   kv_scale: float = 1.0, *, max_seq_len: int, out, lse=None, workspace=None, num_splits: int = 0,
+                   opts: MlaOptions | None = None, stream=None):
+    """mla_decode_tensors: the decode through per-tensor descriptors (element type, shape and strides are
+    checked by the library, strided views included).  out / lse / workspace are caller-owned."""
+    torch = _torch()
+    ws = MlaWorkspace()
+    ws.data = workspace.data_ptr() if workspace is not None else None
+    ws.bytes = workspace.numel() if workspace is not None else 0
+    ws.num_splits = int(num_splits)
+    ws.max_seq_len = int(max_seq_len)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream if q.device.type == "cuda" else None
+    descs = [tensor_desc(t) for t in (q, kv_cache, block_table, seq_lens, out)]
+    ld = tensor_desc(lse) if lse is not None else None
+    _check(lib().mla_decode_tensors(*(ctypes.byref(d) for d in descs[:4]), float(softmax_scale), float(q_scale),
+                                    float(kv_scale), ctypes.byref(descs[4]),
+                                    ctypes.byref(ld) if ld is not None else None, ctypes.byref(ws), stream,
+                                    ctypes.byref(opts) if opts is not None else None))
+    return out, lse
+
+
 def kv_pack_quantize_fp8(latent, rope, kv_scale: float, *, slot_mapping=None, out=None, stream=None):
     """latent [T, 512] bf16 || rope [T, 64] bf16 -> E4M3 rows (uint8 [T, 576] or scattered into `out`)."""
     torch = _torch()
@@ -294,9 +393,14 @@ def kv_pack_quantize_fp8(latent, rope, kv_scale: float, *, slot_mapping=None, ou
         if slot_mapping is not None:
             raise ValueError("pass `out` when scattering through slot_mapping")
         out = torch.empty((T, D_QK), dtype=torch.uint8, device=latent.device)
+    if (out.dtype not in (torch.uint8, torch.float8_e4m3fn) or not out.is_contiguous() or out.dim() < 2
+            or out.shape[-1] != D_QK):
+        raise ValueError("out must be a contiguous uint8 / float8_e4m3fn tensor whose last dimension is 576")
     rows = out.numel() // D_QK
-    if slot_mapping is not None and (slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous()):
-        raise ValueError("slot_mapping must be a contiguous int64 tensor")
+    if slot_mapping is not None and (slot_mapping.dtype != torch.int64 or not slot_mapping.is_contiguous()
+                                     or slot_mapping.numel() != T):
+        raise ValueError("slot_mapping must be a contiguous int64 tensor with one entry per token")
+    _check_device(latent, ("rope", rope), ("out", out), ("slot_mapping", slot_mapping))
     if stream is None:
         stream = torch.cuda.current_stream(latent.device).cuda_stream
     _check(lib().mla_kv_pack_quantize_fp8(latent.data_ptr(), latent.stride(0), rope.data_ptr(), rope.stride(0),

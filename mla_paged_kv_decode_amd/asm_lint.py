@@ -102,7 +102,7 @@ def loop_spills(lines: list[str]) -> list[str]:
     return [f"line {i}: '{s[:60]}' inside the innermost loop" for d, i, s in found if deepest and d == deepest]
 
 
-def lint(asm_text: str, name_part: str = "mla_split_kv_partial") -> dict:
+def lint(asm_text: str, name_part: str = "mla_split_kv") -> dict:
     """{function name: [problems]} for every function whose name contains name_part."""
     out = {}
     for chunk in re.split(r"\n(?=_Z\w+:)", asm_text):

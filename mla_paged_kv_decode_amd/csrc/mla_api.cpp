@@ -52,7 +52,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
-  int F, H_eff, q_len_eff, m_tiles, U, G, xcd_map, u_major, part_bf16;
+  int F, H_eff, q_len_eff, m_tiles, U, G, xcd_map, u_major;
   size_t rows_per_b;
   size_t off_part_o, off_part_lse, off_meta, bytes;
 };
@@ -80,7 +80,6 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int num_cus, const mla_
   pl.q_len_eff = q_len / pl.F;
   pl.m_tiles = (pl.H_eff + mla::kTileM - 1) / mla::kTileM;
   pl.U = pl.q_len_eff * pl.m_tiles;
-  pl.part_bf16 = (opt && opt->partial_fp32) ? 0 : 1;
   long long units_per_seq = max_seq_len > 0 ? (max_seq_len + mla::kPlanUnitKeys - 1) / mla::kPlanUnitKeys : 1;
   if (opt && opt->window > 0) {
     // a window reads at most window + q_len - 1 keys per sequence, from a unit-aligned start
@@ -112,8 +111,10 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int num_cus, const mla_
     pl.bytes = 0;
     pl.off_part_o = pl.off_part_lse = pl.off_meta = 0;
   } else {
+    // partial outputs are sized for fp32 (the plan carries no dtype; E4M3 caches
+    // write bf16 partials into the first half of the region)
     const size_t slots = (size_t)G + (size_t)B;
-    const size_t esz = pl.part_bf16 ? 2 : 4;
+    const size_t esz = 4;
     pl.off_part_o = 0;
     pl.off_part_lse = align_up(slots * pl.rows_per_b * mla::kDv * esz);
     pl.off_meta = pl.off_part_lse + align_up(slots * pl.rows_per_b * sizeof(float));
@@ -183,6 +184,8 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
                 const int32_t* cu_q = nullptr, int32_t total_q = 0) {
   if (opt && (opt->stages < 0 || opt->stages > 2)) return fail(MLA_ERR_SHAPE, "options.stages must be 0, 1 or 2");
   if (opt && opt->window < 0) return fail(MLA_ERR_SHAPE, "options.window must be >= 0 (got %d)", opt->window);
+  if (opt && (opt->kernel < 0 || opt->kernel > 2)) return fail(MLA_ERR_SHAPE, "options.kernel must be 0, 1 or 2");
+  if (opt && (opt->merge < 0 || opt->merge > 1)) return fail(MLA_ERR_SHAPE, "options.merge must be 0 or 1");
   if (!s) return fail(MLA_ERR_NULL, "shape is NULL");
   if (s->dtype != MLA_DTYPE_BF16 && s->dtype != MLA_DTYPE_FP8_E4M3 && s->dtype != MLA_DTYPE_FP16 &&
       s->dtype != MLA_DTYPE_BF16_Q_FP8_KV)
@@ -263,10 +266,15 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
   p.num_pages = s->num_pages;
   p.s_scale_log2 = (float)((double)softmax_scale * (double)q_scale * (double)kv_scale * 1.4426950408889634074);
   p.v_scale = kv_scale;
-  p.part_bf16 = pl.part_bf16;
+  // Partial outputs: bf16 for E4M3 caches (their bar is 5e-2, and the partials' round trip is
+  // the step's largest overhead), fp32 for 16-bit caches (a bf16 rounding of every slice before
+  // the merge would eat most of their 1e-2 bar on rows merged from many slices).
+  const bool e4m3_kv = dt == mla::kFp8 || dt == mla::kMixed;
+  p.part_bf16 = (!(opt && opt->partial_fp32) && e4m3_kv) ? 1 : 0;
   p.window = opt ? opt->window : 0;
   p.cu_q = cu_q;
   p.total_q = total_q;
+  p.kernel = opt ? opt->kernel : 0;
   const int tile = (dt == mla::kFp8 || dt == mla::kMixed) ? 64 : 32;  // keys per LDS tile
   hipStream_t st = (hipStream_t)stream;
   const int stages = opt ? opt->stages : 0;
@@ -289,7 +297,7 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
     c.B = s->batch;
     c.rows_per_b = (int)pl.rows_per_b;
     c.G = pl.G;
-    c.part_bf16 = pl.part_bf16;
+    c.part_bf16 = p.part_bf16;
     c.H = s->num_heads;
     c.q_len = s->q_len;
     c.F = pl.F;
@@ -297,6 +305,7 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
     c.U = pl.U;
     c.cu_q = cu_q;
     c.total_q = total_q;
+    c.merge_kernel = opt ? opt->merge : 0;
     e = mla::launch_combine(c, st);
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "combine kernel launch failed: %s", hipGetErrorString(e));
   }
@@ -393,6 +402,93 @@ int mla_kv_pack_quantize_fp8(const void* latent, int64_t latent_stride, const vo
   hipError_t e = mla::launch_pack_fp8(p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "pack kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+// Tensor-descriptor form: every descriptor is checked against the layout the
+// kernels read (element type, extents, strides), then the call is mla_decode_ex's.
+int mla_decode_tensors(const mla_tensor* q, const mla_tensor* kv_cache, const mla_tensor* block_table,
+                       const mla_tensor* seq_lens, float softmax_scale, float q_scale, float kv_scale,
+                       const mla_tensor* out, const mla_tensor* lse, const mla_workspace* workspace, void* stream,
+                       const mla_options* options) {
+  if (!q || !kv_cache || !block_table || !seq_lens || !out || !workspace)
+    return fail(MLA_ERR_NULL, "q, kv_cache, block_table, seq_lens, out and workspace descriptors must be non-NULL");
+  struct Named {
+    const mla_tensor* t;
+    const char* name;
+    int ndim;
+  };
+  const Named all[] = {{q, "q", 4}, {kv_cache, "kv_cache", 3}, {block_table, "block_table", 2},
+                       {seq_lens, "seq_lens", 1}, {out, "out", 4}, {lse, "lse", 3}};
+  for (const Named& n : all) {
+    if (!n.t) continue;
+    if (n.t->ndim != n.ndim) return fail(MLA_ERR_SHAPE, "%s must have %d dimensions (got %d)", n.name, n.ndim, n.t->ndim);
+    for (int d = 0; d < n.ndim; ++d)
+      if (n.t->shape[d] < 0 || n.t->shape[d] > INT32_MAX)
+        return fail(MLA_ERR_SHAPE, "%s extent %d out of range (%lld)", n.name, d, (long long)n.t->shape[d]);
+  }
+  // element types
+  const int qt = q->dtype, kt = kv_cache->dtype;
+  int dtype;
+  if (qt == kt && (qt == MLA_ELEM_BF16 || qt == MLA_ELEM_FP16 || qt == MLA_ELEM_FP8_E4M3)) {
+    dtype = qt == MLA_ELEM_BF16 ? MLA_DTYPE_BF16 : qt == MLA_ELEM_FP16 ? MLA_DTYPE_FP16 : MLA_DTYPE_FP8_E4M3;
+  } else if (qt == MLA_ELEM_BF16 && kt == MLA_ELEM_FP8_E4M3) {
+    dtype = MLA_DTYPE_BF16_Q_FP8_KV;
+  } else {
+    return fail(MLA_ERR_DTYPE, "q / kv_cache element types %d / %d are not a supported pair", qt, kt);
+  }
+  if (block_table->dtype != MLA_ELEM_INT32 || seq_lens->dtype != MLA_ELEM_INT32)
+    return fail(MLA_ERR_DTYPE, "block_table and seq_lens must be int32");
+  if (out->dtype != MLA_ELEM_BF16) return fail(MLA_ERR_DTYPE, "out must be bf16");
+  if (lse && lse->dtype != MLA_ELEM_FP32) return fail(MLA_ERR_DTYPE, "lse must be fp32");
+  // extents
+  const int64_t B = q->shape[0], QL = q->shape[1], H = q->shape[2];
+  if (q->shape[3] != MLA_D_QK || kv_cache->shape[2] != MLA_D_QK)
+    return fail(MLA_ERR_SHAPE, "q and kv_cache rows must be %d wide", MLA_D_QK);
+  if (block_table->shape[0] != B || seq_lens->shape[0] != B)
+    return fail(MLA_ERR_SHAPE, "block_table must have batch rows and seq_lens batch entries (batch = %lld)",
+                (long long)B);
+  if (out->shape[0] != B || out->shape[1] != QL || out->shape[2] != H || out->shape[3] != MLA_D_V)
+    return fail(MLA_ERR_SHAPE, "out must be [batch, q_len, num_heads, %d]", MLA_D_V);
+  if (lse && (lse->shape[0] != B || lse->shape[1] != QL || lse->shape[2] != H))
+    return fail(MLA_ERR_SHAPE, "lse must be [batch, q_len, num_heads]");
+  // strides: packed row-major everywhere; a dimension of extent 1 may carry any stride
+  auto packed = [](const mla_tensor* t) {
+    int64_t want = 1;
+    for (int d = t->ndim - 1; d >= 0; --d) {
+      if (t->shape[d] != 1 && t->stride[d] != want) return false;
+      want *= t->shape[d];
+    }
+    return true;
+  };
+  for (const Named& n : all)
+    if (n.t && !packed(n.t))
+      return fail(MLA_ERR_STRIDE, "%s must be packed row-major (its strides are not)", n.name);
+  if (!q->data || !kv_cache->data || !block_table->data || !seq_lens->data || !out->data || (lse && !lse->data))
+    return fail(MLA_ERR_NULL, "a tensor descriptor has a NULL data pointer");
+  mla_shape s{};
+  s.batch = (int32_t)B;
+  s.q_len = (int32_t)QL;
+  s.num_heads = (int32_t)H;
+  s.num_pages = (int32_t)kv_cache->shape[0];
+  s.page_size = (int32_t)kv_cache->shape[1];
+  s.max_pages = (int32_t)block_table->shape[1];
+  s.max_seq_len = workspace->max_seq_len;
+  s.dtype = dtype;
+  if (workspace->num_splits != 0 && s.batch > 0) {
+    int rc = check_plan_args(s.batch, s.q_len, s.num_heads, s.max_seq_len);
+    if (rc) return rc;
+    int dev = 0, cus = 0;
+    rc = device_cus(&dev, &cus);
+    if (rc) return rc;
+    Plan pl;
+    cached_plan(dev, cus, s.batch, s.q_len, s.num_heads, s.max_seq_len, options, &pl);
+    if (pl.G != workspace->num_splits)
+      return fail(MLA_ERR_WORKSPACE, "workspace was planned for %d splits, this shape plans %d", workspace->num_splits,
+                  pl.G);
+  }
+  return decode_impl(&s, q->data, kv_cache->data, (const int32_t*)block_table->data, (const int32_t*)seq_lens->data,
+                     softmax_scale, q_scale, kv_scale, out->data, lse ? (float*)lse->data : nullptr, workspace->data,
+                     workspace->bytes, stream, options);
 }
 
 const char* mla_last_error(void) { return g_last_error.c_str(); }

@@ -44,7 +44,9 @@ struct PartialParams {
   int32_t window;            // sliding window in keys (0: none)
   const int32_t* cu_q;       // ragged batch: [B+1] cumulative new-token counts (device), or nullptr
   int32_t total_q;           // ragged batch: token rows of q / out
+  int32_t kernel;            // E4M3: 1 the four-wave kernel, 2 the role-specialised kernel, 0 the default
 };
+constexpr int kDefaultFp8Kernel = 2;
 
 struct CombineParams {
   const void* part_o;
@@ -58,6 +60,7 @@ struct CombineParams {
   int32_t F, q_len_eff, U;    // fold factor, query groups, workgroup rows (meta is [U][B][2], then int64 T[U])
   const int32_t* cu_q;        // ragged batch: [B+1] cumulative new-token counts, or nullptr
   int32_t total_q;
+  int32_t merge_kernel;       // rows over many slices: 0 the wide merge (a wave per row quarter), 1 a workgroup per row
 };
 
 struct PackParams {

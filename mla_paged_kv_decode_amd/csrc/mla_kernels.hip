@@ -11,7 +11,8 @@
 //    relative to a per-row reference fixed at the row's first visible tile (a
 //    segment is recomputed in the rare case a row max outgrows it); the FP8
 //    probabilities carry a per-row power-of-two block scale through the MFMA's
-//    scale operand.  Writes the final bf16 O / fp32
+//    scale operand; O is normalised by the sum of the rounded probabilities (the
+//    weights the PV product used), the LSE by the exact sum.  Writes the final bf16 O / fp32
 //    LSE when the slice holds the whole sequence, else a partial (O, LSE).
 //    (Split-KV partial kernel: TokenSpeed MLA article, section 2; query-token
 //    folding: section 3.)
@@ -192,6 +193,25 @@ __device__ __forceinline__ void qk_mfma_h16(v16f& acc, const v4i& a, const v4i& 
     }
   }
 }
+// MFMA with its accumulator in VGPRs, through asm (the role-specialised FP8
+// kernel keeps every value in VGPRs, so that its two roles share one register
+// budget).  The compiler models neither its latency nor its hazards: a
+// VALU-written operand needs two wait states before it (lead), and the caller
+// pads with s_nop (mfma_drain) after the last MFMA before the accumulators are
+// read or rewritten by anything but another MFMA.
+__device__ __forceinline__ void mfma_f8_v(v16f& acc, const v8i& a, const v8i& b, int scale_b, bool lead) {
+  if (lead) {
+    asm volatile("s_nop 1\n\tv_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+                 : "+v"(acc)
+                 : "v"(a), "v"(b), "v"(127), "v"(scale_b));
+  } else {
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+                 : "+v"(acc)
+                 : "v"(a), "v"(b), "v"(127), "v"(scale_b));
+  }
+}
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 // Scheduling fences.  The instruction selector places pure arithmetic next to
 // its uses, regardless of where the source puts it; routing a slot's inputs
 // and outputs through empty volatile asm statements pins that work between
@@ -273,6 +293,16 @@ __device__ __forceinline__ uint32_t pack_p16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2h));
   } else {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
+  }
+}
+// The two probabilities of a packed word as the PV product sees them, summed in fp32.
+template <int DT>
+__device__ __forceinline__ float sum_p16x2(uint32_t w) {
+  if constexpr (DT == kFp16) {
+    const v2f f = __builtin_convertvector(__builtin_bit_cast(v2h, w), v2f);
+    return f[0] + f[1];
+  } else {
+    return __builtin_bit_cast(float, w << 16) + __builtin_bit_cast(float, w & 0xffff0000u);
   }
 }
 template <int DT>
@@ -462,6 +492,11 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   v16f o[16];
   float m_ref = -INFINITY;  // reference the accumulators are relative to (log2 units)
   float l_acc = 0.f;        // this lane's share of sum exp2(s - m_ref)
+  float l_acc_r = 0.f;      // the same over P as rounded for the PV MFMA (E4M3): normalises O
+  // 16-bit P keeps that rounded sum in LDS instead (one slot per lane, in the E4M3 P-scale
+  // area these kernels leave unused): the register-bound loop holds no second sum
+  typedef __attribute__((address_space(3))) float lds_f32;
+  auto lr_slot = [&]() { return (lds_f32*)(smem + kPScaleOffset + 256 * wave + 4 * lane); };
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     o[i] = v16f{0};
@@ -665,6 +700,8 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
       bool ovf = false;
       m_ref = m_init;
       l_acc = 0.f;
+      l_acc_r = 0.f;
+      if constexpr (DT != kFp8) *lr_slot() = 0.f;
       if (attempt > 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -707,7 +744,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         int pa[4], pb[4];       // fp8 P words: keys 0..31 and 32..63
         float pe_off = 0.f;     // exp2 offset of the tile whose P is being built
         int pe_e = 0;           // its power-of-two scale
-        float lsum = 0.f, mx_raw = -INFINITY, p_hold = 0.f;
+        float lsum = 0.f, lsum_r = 0.f, mx_raw = -INFINITY, p_hold = 0.f;
         int w_hold = 0;
 
         // softmax, first half (PV slots 0..15): row max over the tile (tree, two
@@ -724,15 +761,22 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         // (fma in one slot, exp2 in the next, sum and fp8 pack in the one after),
         // so the VALU work inside a slot has no dependency chain to wait on.
         float ya[2], yb[2], qa[2], qb[2];  // pair stages: fma results, exp2 results
-        auto pack_pair = [&](float p0, float p1, int pair, int* words) {
+        // Returns the sum of the two values as rounded to E4M3: O is normalised by the sum of
+        // the weights the PV product used, so they sum to one (a row that sees one key returns
+        // that key's V exactly); the LSE keeps the exact sum.
+        auto pack_pair = [&](float p0, float p1, int pair, int* words) -> float {
           // pair j holds elements 2j, 2j+1: even pairs fill the low half of word j/2, odd pairs the high
+          v2f r;
           if ((pair & 1) == 0) {
             w_hold = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
             fence_v(w_hold);
+            r = __builtin_amdgcn_cvt_pk_f32_fp8(w_hold, false);
           } else {
             words[pair >> 1] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, w_hold, true);
             fence_v(words[pair >> 1]);
+            r = __builtin_amdgcn_cvt_pk_f32_fp8(words[pair >> 1], true);
           }
+          return r[0] + r[1];
         };
         auto part_a = [&](int slot, int key0, bool need_mask) {
           if (slot == 0) {
@@ -776,6 +820,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             pe_e = e;
             pe_off = mref - (float)e;
             lsum = 0.f;
+            lsum_r = 0.f;
             fence_v(pe_off);
             fence_v(pe_e);
           } else if (slot >= 4 && slot < 14) {
@@ -786,8 +831,9 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             if (t >= 2) {
               const int j = t - 2;
               lsum += qa[j & 1] + qb[j & 1];
+              lsum_r += pack_pair(qa[j & 1], qb[j & 1], j, pa);
               fence_v(lsum);
-              pack_pair(qa[j & 1], qb[j & 1], j, pa);
+              fence_v(lsum_r);
             }
             if (t >= 1 && t <= 8) {
               const int j = t - 1;
@@ -809,14 +855,15 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         auto part_b = [&](int slot) {
           fence_v(hb);  // (in place: no copy)
           if (slot >= 2) {
-            const int k = slot - 2;  // sum and pack element k
+            const int k = slot - 2;  // sum and pack element k (the rounded sum pair by pair)
             lsum += qa[k & 1];
             fence_v(lsum);
             if ((k & 1) == 0) {
               p_hold = qa[k & 1];
               fence_v(p_hold);
             } else {
-              pack_pair(p_hold, qa[k & 1], k >> 1, pb);
+              lsum_r += pack_pair(p_hold, qa[k & 1], k >> 1, pb);
+              fence_v(lsum_r);
             }
           }
           if (slot >= 1 && slot <= 16) {
@@ -830,7 +877,9 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           }
           if (slot == 17) {
             l_acc += __builtin_ldexpf(lsum, -pe_e);
+            l_acc_r += __builtin_ldexpf(lsum_r, -pe_e);
             fence_v(l_acc);
+            fence_v(l_acc_r);
           }
         };
         // S^T = K Q^T for one tile: two 32-key blocks, K = 576 in 9 steps of 64
@@ -1087,6 +1136,15 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             pb[g4 >> 1][2 * (g4 & 1) + 1] = (int)pack_p16x2<CDT>(pv4[2], pv4[3]);
           } else if (i == 7) {
             l_acc += lsum;
+            // the sum of P as rounded into the operand words (summed once they are all packed, so
+            // no second running sum is held across the chunks)
+            float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              r0 += sum_p16x2<CDT>((uint32_t)pb[0][w]);
+              r1 += sum_p16x2<CDT>((uint32_t)pb[1][w]);
+            }
+            __hip_atomic_fetch_add(lr_slot(), r0 + r1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           }
         };
         if constexpr (XPV) {
@@ -1265,9 +1323,11 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
     const int ne = lane & 31, he = lane >> 5;
     const float l_tot = xor32_sum(l_acc);
     const bool has = l_tot > 0.f;
-    const float inv = has ? p.v_scale / l_tot : 0.f;
+    // O is normalised by the sum of the weights the PV product used (P as rounded to its
+    // operand type), the LSE by the exact sum
+    const float l_norm = xor32_sum(DT == kFp8 ? l_acc_r : *lr_slot());
+    const float inv = has && l_norm > 0.f ? p.v_scale / l_norm : 0.f;
     const float lse_v = has ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
-    typedef __attribute__((address_space(3))) float lds_f32;
     lds_f32* s_inv = (lds_f32*)(smem + kPOffset);
     lds_barrier();  // every wave is done with the KV ring and the P buffer
     if (he == 0) s_inv[32 * wave + ne] = inv;
@@ -1360,7 +1420,8 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   const int ne = lane & 31, he = lane >> 5;
   const float l_tot = xor32_sum(l_acc);
   const bool has = l_tot > 0.f;
-  const float inv = has ? p.v_scale / l_tot : 0.f;
+  const float l_norm = xor32_sum(*lr_slot());  // the rounded P's sum, as in the other epilogue
+  const float inv = has && l_norm > 0.f ? p.v_scale / l_norm : 0.f;
   const float lse_v = has ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
   const bool f32out = !sg.single && !p.part_bf16;
   const int wrow0 = mt * kTileM + 32 * wave;  // first row of this wave
@@ -1430,16 +1491,545 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   }
 }
 
-template <int DT, bool FAST, bool WIN, bool XPV>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-mla_split_kv_partial(PartialParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kLdsBytes];
-  __shared__ int s_flag[4];
-  lds_t* smem = (lds_t*)smem_raw;
-  constexpr int UK = Traits<DT>::kTile;  // keys per work unit
+// ---------------------------------------------------------------------------
+// FP8 split-KV segment with specialised waves: twelve waves, three per SIMD
+// (168 registers each, all VGPRs).
+//   score waves 0-3, one per SIMD: row block sr = wave (32 query rows) against
+//     the whole 64-key tile: 18 MFMAs (two 32-key blocks x 9 K-steps of 64),
+//     then the softmax; their Q block lives in 72 VGPRs.  Each owns its rows'
+//     softmax state: a reference m_ref fixed at the row's first visible tile,
+//     P scaled per tile so its largest value lands in (128, 256], the scale
+//     2^-e handed to the PV MFMA as its E8M0 block scale, the row sums (exact,
+//     for the LSE; over the rounded P, to normalise O).
+//   PV waves 4-11: O^T for latent dims [64 pw, 64 pw + 64), pw = wave - 4, and
+//     all 128 rows: 8 MFMAs (2 dim blocks x 4 row blocks) per tile, their output
+//     block in 128 VGPRs; waves 4-7 also issue the tile loads.
+// Per tile t, phase A: the score waves run the scores and softmax of tile t (at
+// raised priority while their MFMAs issue), the PV waves the PV of tile t-1, so
+// the score waves' softmax overlaps the PV MFMAs on every SIMD.  [barrier]
+// Phase B: the score waves publish P(t), its scales and the rows' rescale
+// factors; the stage of tile t-1 is reissued for tile t+3.  [barrier, tile t+1
+// landed]  Three tiles stay in flight.  A row whose max outgrows its reference
+// by more than kTau moves the reference (one pass, no recomputation): the score
+// wave scales its row sums by 2^(old - new) and publishes that factor, the PV
+// waves scale the row's output accumulators by it before adding the tile.
+// ---------------------------------------------------------------------------
+constexpr int kThreadsR = 768;
+constexpr int kRDummy = kStages * kStageBytes;  // 1 KiB: destination of dummy-tile loads
+constexpr int kRP = kRDummy + 1024;              // P codes: [row block 4][half 2][lane 64][16 bytes]
+constexpr int kRScale = kRP + 8192;              // E8M0 scale codes: [row block 4][lane 64] int32
+constexpr int kRResc = kRScale + 1024;           // per-row rescale factor of the tile: [row block 4][row 32] fp32
+constexpr int kRBt = kRResc + 512;                // block-table entries of the segment
+constexpr int kRLdsBytes = kRBt + 4 * kBtEntries;
+static_assert(kRLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases in SGPRs
+// SCORE: the code of the score waves (true) or of the PV waves (false).  The two
+// are separate instantiations, called from separate branches of the kernel, so
+// that a wave's registers hold only its own role's state; both run the same
+// sequence of workgroup barriers.
+template <bool FAST, bool WIN, bool SCORE>
+__device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t* smem, const SegmentCtx& sg, int g,
+                                                  int mt, int wave, int lane) {
+  constexpr int TILE = 64;
+  constexpr int RB = 576;
+  constexpr int CH = 36;
+  typedef __attribute__((address_space(3))) int lds_i32;
+  typedef __attribute__((address_space(3))) float lds_f32;
+
+  asm volatile("" : "+v"(lane));
+  asm volatile("" : "+s"(wave));
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int sr = wave & 3;                         // score role: row block
+  const int pw = wave - 4;                         // PV role: latent dims [64 pw, +64)
+  const bool dma_wave = !SCORE && wave < 8;        // issue the tile loads (PV waves 4-7)
+  const int dw = wave - 4;                         // their index
+  cint_t* seq_lens = (cint_t*)p.seq_lens;
+  const int L = max(seq_lens[sg.b], 0);
+  int qlen_b, tok0;
+  seq_tokens(p, sg.b, qlen_b, tok0);
+  const int gF = g * p.F;
+  const int rows_valid = min(p.H_eff, max(qlen_b - gF, 0) * p.H);
+  if (rows_valid <= mt * kTileM) return;
+  const int n_gmax = min(max(L - qlen_b + gF + p.F, 0), L);
+  const int window = WIN ? p.window : 0;
+  const int kbase = seq_key0<TILE>(L, qlen_b, window);
+  const int k0 = kbase + sg.u0 * TILE;
+  const int k1 = min(kbase + sg.u1 * TILE, n_gmax);
+
+  // the score wave's row (row n of block sr)
+  const int m = mt * kTileM + 32 * sr + n;
+  const bool row_valid = m < rows_valid;
+  const int n_row = row_valid ? min(max(L - qlen_b + gF + m / p.H + 1, 0), L) : 0;
+  const int lim = min(n_row, k1);
+  const int lo = window > 0 ? max(n_row - window, 0) : 0;
+  auto mask_bounds = [&](int& lo_m, uint32_t& vis_m) {
+    if constexpr (WIN) {
+      int nr = n_row;
+      asm volatile("" : "+v"(nr));
+      lo_m = window > 0 ? max(nr - window, 0) : 0;
+      vis_m = (uint32_t)max(min(nr, k1) - lo_m, 0);
+    } else {
+      lo_m = 0;
+      vis_m = (uint32_t)lim;
+    }
+  };
+  const size_t rows_per_b = (size_t)p.q_len * p.H;
+  const size_t out_row0 = (size_t)tok0 * p.H;
+
+  v8i qreg[SCORE ? 9 : 1];  // score waves: Q of the row block (B operand, K-steps of 64)
+  v16f o[SCORE ? 1 : 8];     // PV waves: o[4 j + rb] = dims 64 pw + 32 j .. + 31 of row block rb
+  float m_ref = -INFINITY;
+  float l_acc = 0.f, l_acc_r = 0.f;
+  if constexpr (!SCORE) {
+    // zeros made here (opaque): a hoisted constant block would be kept, or spilled, across segments
+    float z = 0.f;
+    asm volatile("" : "+v"(z));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = v16f{z, z, z, z, z, z, z, z, z, z, z, z, z, z, z, z};
+  }
+
+  if (k1 > k0) {
+    const int ntiles = (k1 - k0 + TILE - 1) / TILE;
+    const int pmask = p.page_size - 1;
+    cint_t* bt = (cint_t*)p.block_table + (size_t)sg.b * p.max_pages;
+    const int plast = min((k1 - 1) >> p.page_shift, p.max_pages - 1);
+    const uint32_t smem_base = lds_addr(smem);
+
+    int bt_base = 0;
+    auto bt_fill = [&](int first) {
+      bt_base = first;
+      int v = 0;
+      if (dma_wave) v = bt[min(first + 64 * dw + lane, plast)];
+      lds_barrier();
+      if (dma_wave) *(lds_i32*)(smem + kRBt + 4 * (64 * dw + lane)) = v;
+      lds_barrier();
+    };
+    // (uniform: kept in scalar registers from the start)
+    auto page_raw = [&](int pidx) -> int {
+      return __builtin_amdgcn_readfirstlane(*(const lds_i32*)(smem + kRBt + 4 * (min(pidx, plast) - bt_base)));
+    };
+    auto clamp_page = [&](int pg) -> int { return min(max(__builtin_amdgcn_readfirstlane(pg), 0), p.num_pages - 1); };
+    const uint8_t* d_base = p.kv;
+    uint32_t d_m0 = smem_base, d_step = 1024;
+    int d_key0 = k0, d_pidx0 = 0;
+    int d_pg0 = 0, d_pg1 = 0, d_pg2 = 0, d_pg3 = 0;
+    int pf0 = 0, pf1 = 0, pf2 = 0, pf3 = 0;
+    auto prefetch_pages = [&](int tt) {
+      const int pidx0 = (k0 + tt * TILE) >> p.page_shift;
+      constexpr int kFillTiles = FAST ? kBtEntries : (kBtEntries - 3) / 4;
+      if (tt > 0 && tt % kFillTiles == 0) bt_fill(pidx0);
+      pf0 = page_raw(pidx0);
+      if constexpr (!FAST) {
+        pf1 = page_raw(pidx0 + 1);
+        pf2 = page_raw(pidx0 + 2);
+        pf3 = page_raw(pidx0 + 3);
+      }
+    };
+    // every wave sets up (the block-table refill inside is a workgroup barrier); the DMA waves issue
+    auto dma_setup = [&](int tt) {
+      if (tt < ntiles) {
+        const int key0 = k0 + tt * TILE;
+        d_m0 = smem_base + (uint32_t)((tt % kStages) * kStageBytes);
+        d_step = 1024;
+        d_key0 = key0;
+        d_pidx0 = key0 >> p.page_shift;
+        if constexpr (FAST) {
+          d_base = p.kv + ((size_t)clamp_page(pf0) * p.page_size + (key0 & pmask)) * RB;
+        } else {
+          d_pg0 = clamp_page(pf0);
+          d_pg1 = clamp_page(pf1);
+          d_pg2 = clamp_page(pf2);
+          d_pg3 = clamp_page(pf3);
+        }
+        if (tt + 1 < ntiles) prefetch_pages(tt + 1);
+      } else {
+        d_m0 = smem_base + (uint32_t)kRDummy;
+        d_step = 0;
+      }
+    };
+    auto dma_issue = [&](int kk) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int slot = 64 * (dw + 4 * kk) + ln;
+      const int row = slot / CH;
+      const uint32_t off = (uint32_t)(row * RB + ((slot - row * CH) ^ swz<kFp8>(row)) * 16);
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(d_m0 + d_step * (uint32_t)(dw + 4 * kk));
+      if constexpr (FAST) {
+        dma16_sbase(off, d_base, m0);
+      } else {
+        const int key = d_key0 + row;
+        const int rel = (key >> p.page_shift) - d_pidx0;
+        const int g0 = __builtin_amdgcn_readfirstlane(d_pg0), g1 = __builtin_amdgcn_readfirstlane(d_pg1);
+        const int g2 = __builtin_amdgcn_readfirstlane(d_pg2), g3 = __builtin_amdgcn_readfirstlane(d_pg3);
+        const int pg = rel == 0 ? g0 : rel == 1 ? g1 : rel == 2 ? g2 : g3;
+        const uint8_t* src = p.kv + ((size_t)pg * p.page_size + (key & pmask)) * RB + (off - (uint32_t)(row * RB));
+        dma16_vaddr(src, m0);
+      }
+    };
+    auto issue_tile = [&](int tt) {
+      dma_setup(tt);
+      if (dma_wave) {
+#pragma unroll
+        for (int kk = 0; kk < kDmaPerWave; ++kk) dma_issue(kk);
+      }
+    };
+    // the DMA waves wait for their loads of the next tile (the two younger tiles stay in
+    // flight), every wave for its LDS writes; then the barrier
+    auto wait_next = [&]() {
+      if (dma_wave) {
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * kDmaPerWave) : "memory");
+      } else {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+    };
+    auto stage = [&](int t) -> const lds_t* { return smem + (t % kStages) * kStageBytes; };
+    auto zero_tail = [&](int t) {
+      const int nvalid = k1 - (k0 + t * TILE);
+      if (nvalid < TILE) {
+        lds_t* z = smem + (t % kStages) * kStageBytes + nvalid * RB;
+        const int nchunks = (TILE - nvalid) * (RB / 16);
+        int zr = 0;
+        asm volatile("" : "+v"(zr));  // (a hoisted zero vector would be kept across the loop)
+        for (int i = 64 * wave + lane; i < nchunks; i += kThreadsR) *(lds_v4i*)(z + 16 * i) = v4i{zr, zr, zr, zr};
+        lds_barrier();
+      }
+    };
+
+    // score waves: keys inside [lo_max, lim_min) of every row need no mask
+    int lim_min = lim, lo_max = lo;
+#pragma unroll
+    for (int o2 = 32; o2 > 0; o2 >>= 1) {
+      lim_min = min(lim_min, __shfl_xor(lim_min, o2, 64));
+      lo_max = max(lo_max, __shfl_xor(lo_max, o2, 64));
+    }
+    lim_min = __builtin_amdgcn_readfirstlane(lim_min);
+    lo_max = __builtin_amdgcn_readfirstlane(lo_max);
+    auto tile_needs_mask = [&](int key0) { return key0 + TILE > lim_min || key0 < lo_max; };
+
+    {
+      bt_fill(k0 >> p.page_shift);  // (its first barrier: the previous use of LDS is over)
+      prefetch_pages(0);
+
+      // ---------------- score role ----------------
+      v16f s0, s1;
+      int pa[4], pb[4];
+      int sc_code = 127;
+      float resc = 1.f;  // this tile's reference change of the row (1: none)
+      auto qk = [&](const lds_t* st) {
+        int ka = (32 * 0 + n) * RB + (((2 * hh) ^ ((n >> 2) & 3)) * 16);
+        asm volatile("" : "+v"(ka));
+        auto kread = [&](int c, int kb) -> v8i {
+          const int a0 = ka + 32 * RB * kb;
+          const v4i x = *(const lds_v4i*)(st + a0 + 64 * c);
+          const v4i y = *(const lds_v4i*)(st + (a0 ^ 16) + 64 * c);
+          return v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        };
+        v8i kb[3];
+        kb[0] = kread(0, 0);
+        kb[1] = kread(0, 1);
+#pragma unroll
+        for (int i = 0; i < 18; ++i) {
+          if (i + 2 < 18) kb[(i + 2) % 3] = kread((i + 2) >> 1, (i + 2) & 1);
+          if (i & 1) {
+            if (i == 1) qk_mfma_f8_first(s1, kb[i % 3], qreg[i >> 1]);
+            else qk_mfma_f8(s1, kb[i % 3], qreg[i >> 1], i == 17);
+          } else {
+            if (i == 0) qk_mfma_f8_first(s0, kb[i % 3], qreg[i >> 1]);
+            else qk_mfma_f8(s0, kb[i % 3], qreg[i >> 1], i == 16);
+          }
+        }
+      };
+      auto softmax = [&](int key0, bool need_mask) {
+        if (need_mask) {
+          int lo_m;
+          uint32_t vis_m;
+          mask_bounds(lo_m, vis_m);
+          int kb = 4 * hh;
+          asm volatile("" : "+v"(kb));
+          kb += key0 - lo_m;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            if ((uint32_t)(kb + 8 * (r >> 2) + (r & 3)) >= vis_m) s0[r] = -INFINITY;
+            if ((uint32_t)(kb + 32 + 8 * (r >> 2) + (r & 3)) >= vis_m) s1[r] = -INFINITY;
+          }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+        const float rm = xor32_max(mx * p.s_scale_log2);  // row max of the tile, log2 units
+        // The reference is fixed at the row's first visible tile and moves only when a tile's
+        // max outgrows it by more than kTau: then everything accumulated so far is scaled by
+        // 2^(old - new) (the row sums here, the output accumulators by the PV waves).
+        resc = 1.f;
+        if (m_ref == -INFINITY) {
+          m_ref = rm;
+        } else if (rm > m_ref + kTau) {
+          resc = __builtin_amdgcn_exp2f(m_ref - rm);
+          m_ref = rm;
+          l_acc *= resc;
+          l_acc_r *= resc;
+        }
+        const float mref = m_ref > -INFINITY ? m_ref : 0.f;
+        int e = 0;
+        if (rm > -INFINITY) e = 8 - (int)ceilf(rm - mref);
+        e = min(max(e, -120), 120);
+        const float off = mref - (float)e;
+        float lsum = 0.f, lsum_r = 0.f;
+        auto four = [&](const v16f& sv, int w2) -> int {
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * w2 + 0], p.s_scale_log2, -off));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * w2 + 1], p.s_scale_log2, -off));
+          const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * w2 + 2], p.s_scale_log2, -off));
+          const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * w2 + 3], p.s_scale_log2, -off));
+          int wv = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+          wv = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, wv, true);
+          lsum += (e0 + e1) + (e2 + e3);
+          const v2f r0 = __builtin_amdgcn_cvt_pk_f32_fp8(wv, false);
+          const v2f r1 = __builtin_amdgcn_cvt_pk_f32_fp8(wv, true);
+          lsum_r += (r0[0] + r0[1]) + (r1[0] + r1[1]);
+          return wv;
+        };
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          pa[w2] = four(s0, w2);
+          pb[w2] = four(s1, w2);
+        }
+        l_acc += __builtin_ldexpf(lsum, -e);
+        l_acc_r += __builtin_ldexpf(lsum_r, -e);
+        sc_code = 127 - e;
+      };
+      auto publish = [&]() {
+        *(lds_v4i*)(smem + kRP + 2048 * sr + 16 * lane) = v4i{pa[0], pa[1], pa[2], pa[3]};
+        *(lds_v4i*)(smem + kRP + 2048 * sr + 1024 + 16 * lane) = v4i{pb[0], pb[1], pb[2], pb[3]};
+        *(lds_i32*)(smem + kRScale + 256 * sr + 4 * lane) = sc_code;
+        if (hh == 0) *(lds_f32*)(smem + kRResc + 128 * sr + 4 * n) = resc;
+      };
+      auto score_tile = [&](int t) {
+        const int key0 = k0 + t * TILE;
+        __builtin_amdgcn_s_setprio(2);  // the score chain is the tile's critical path
+        qk(stage(t));
+        __builtin_amdgcn_s_setprio(0);
+        softmax(key0, tile_needs_mask(key0));
+      };
+
+      // ---------------- PV role ----------------
+      int vaddr0;
+      {
+        const int grp = lane >> 4, hs = grp >> 1, dsub = grp & 1, uu = lane & 15, rr = uu >> 1, c8 = uu & 1;
+        const int kbr = 8 * (rr >> 2) + 4 * hs + (rr & 3);
+        const int s8 = (2 * (rr >> 2) + hs) & 3;
+        vaddr0 = kbr * RB + ((dsub ^ s8) * 16) + 8 * c8;  // chunk pair partner: ^ 32
+      }
+      auto pv_tile = [&](int t) {
+        const lds_t* st = stage(t);
+        int va = vaddr0 + 64 * pw;
+        asm volatile("" : "+v"(va));
+        auto vread = [&](int base) -> v8i {
+          const v2i r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(st + base));
+          const v2i r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(st + base + 16 * RB));
+          const v2i r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(st + base + 32 * RB));
+          const v2i r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(st + base + 48 * RB));
+          return v8i{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+        };
+        // rows whose reference moved with this tile: rescale what they hold first
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const float f = *(const lds_f32*)(smem + kRResc + 128 * rb + 4 * (lane & 31));
+          if (__builtin_amdgcn_ballot_w64(f != 1.f) != 0) {
+            o[rb] *= f;
+            o[4 + rb] *= f;
+          }
+        }
+        const v8i v0 = vread(va), v1 = vread(va ^ 32);
+        // The four row blocks' P stream past the two V operands, one at a time: each read's
+        // address is made opaque where it is used, so that the reads are neither merged nor
+        // hoisted together (32 more live registers than the budget allows).
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          int pa_ = 16 * lane;
+          asm volatile("" : "+v"(pa_));
+          const v4i x = *(const lds_v4i*)(smem + kRP + 2048 * rb + pa_);
+          const v4i y = *(const lds_v4i*)(smem + kRP + 2048 * rb + 1024 + pa_);
+          const int scb = *(const lds_i32*)(smem + kRScale + 256 * rb + (pa_ >> 2));
+          const v8i pr = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+          o[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v0, pr, o[rb], 0, 0, 0, 127, 0, scb);
+          o[4 + rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v1, pr, o[4 + rb], 0, 0, 0, 127, 0, scb);
+          // the MFMAs stay here (left alone, the compiler sinks them past the barrier that
+          // follows, keeping every P operand live across it)
+          asm volatile("" : "+v"(o[rb]), "+v"(o[4 + rb]));
+        }
+      };
+
+      // ---- prologue: Q through ring stages 2-3, tiles 0 and 1 ----
+      constexpr int kQDma = 32 * kDqk / 1024;  // 18 one-KiB loads per DMA wave (one row block)
+      if (dma_wave) {
+        const uint8_t* qblk = p.q + ((size_t)tok0 + gF) * p.H * kDqk;
+        const uint32_t qlds = smem_base + (uint32_t)(2 * kStageBytes + dw * 32 * kDqk);
+        int qlane = lane;
+        asm volatile("" : "+v"(qlane));
+#pragma unroll
+        for (int kk = 0; kk < kQDma; ++kk) {
+          const int o_ = 1024 * kk + 16 * qlane;
+          const int qn = o_ / kDqk;
+          const int mrow = mt * kTileM + 32 * dw + qn;
+          const int src_row = mrow < rows_valid ? mrow : 0;
+          dma16_vaddr(qblk + (size_t)src_row * kDqk + (o_ - qn * kDqk),
+                      __builtin_amdgcn_readfirstlane(qlds + 1024u * (uint32_t)kk));
+        }
+      }
+      issue_tile(0);
+      issue_tile(1);
+      if (dma_wave) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kDmaPerWave) : "memory");  // Q has landed
+      lds_barrier();
+      if constexpr (SCORE) {
+        const lds_t* qs = smem + 2 * kStageBytes + sr * 32 * kDqk + n * kDqk + 32 * hh;
+        const int keep = row_valid ? -1 : 0;
+#pragma unroll
+        for (int c = 0; c < 9; ++c) {
+          const v4i x0 = *(const lds_v4i*)(qs + 64 * c) & keep;
+          const v4i x1 = *(const lds_v4i*)(qs + 64 * c + 16) & keep;
+          qreg[c] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        }
+      }
+      // tile 0 has landed and every score wave holds its Q: stages 2-3 may be refilled
+      if (dma_wave) {
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaPerWave) : "memory");
+      } else {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+      if (ntiles == 1) zero_tail(0);
+      issue_tile(2);
+      issue_tile(3);
+      if constexpr (SCORE) score_tile(0);
+      lds_barrier();
+      if constexpr (SCORE) publish();
+      wait_next();  // P(0) visible, tile 1 landed
+
+      for (int t = 1; t < ntiles; ++t) {
+        if (t == ntiles - 1) zero_tail(t);
+        if constexpr (SCORE) {
+          score_tile(t);
+        } else {
+          pv_tile(t - 1);
+        }
+        lds_barrier();  // PV of tile t-1 is done: the P buffer and the stage of tile t-1 are free
+        if constexpr (SCORE) publish();
+        issue_tile(t + 3);
+        wait_next();  // P(t) visible, tile t+1 landed
+      }
+      if constexpr (!SCORE) pv_tile(ntiles - 1);
+      // the dummy loads must land before LDS is reused
+      if (dma_wave) {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      }
+    }
+  }
+
+  // ---- epilogue: the score waves publish 1/l and write the LSE; the PV waves stage O ----
+  asm volatile("" : "+v"(lane));
+  const int ne = lane & 31, he = lane >> 5;
+  lds_f32* s_inv = (lds_f32*)(smem + kRScale);
+  lds_barrier();  // every wave is done with the ring, P and the scales
+  const int row0 = mt * kTileM;
+  if constexpr (SCORE) {
+    const float l_tot = xor32_sum(l_acc);
+    const float l_r = xor32_sum(l_acc_r);
+    const bool has = l_tot > 0.f && l_r > 0.f;
+    const float inv = has ? p.v_scale / l_r : 0.f;
+    const float lse_v = has ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
+    if (he == 0) s_inv[32 * sr + ne] = inv;
+    const int m_l = row0 + 32 * sr + ne;
+    if (he == 0 && m_l < rows_valid) {
+      const size_t rowb = (size_t)gF * p.H + (size_t)m_l;
+      if (sg.single) {
+        if (p.lse != nullptr) p.lse[out_row0 + rowb] = lse_v;
+      } else {
+        p.part_lse[(size_t)sg.slot * rows_per_b + rowb] = lse_v;
+      }
+    }
+  }
+  lds_barrier();
+  float invr[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) invr[rb] = s_inv[32 * rb + ne];
+  const bool f32out = !sg.single && !p.part_bf16;
+  if (!f32out) {
+    uint16_t* dst = sg.single ? p.out + out_row0 * kDv : (uint16_t*)p.part_o + (size_t)sg.slot * rows_per_b * kDv;
+    if constexpr (!SCORE) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int row = 32 * rb + ne, col = 64 * pw + 32 * j + 8 * gq + 4 * he;
+            const v16f& acc = o[4 * j + rb];
+            const v2i wv = v2i{(int)pack_bf16x2(acc[4 * gq + 0] * invr[rb], acc[4 * gq + 1] * invr[rb]),
+                               (int)pack_bf16x2(acc[4 * gq + 2] * invr[rb], acc[4 * gq + 3] * invr[rb])};
+            *(lds_v2i*)(smem + row * kEpiPitch + 2 * col) = wv;
+          }
+        }
+      }
+    }
+    lds_barrier();
+    if constexpr (!SCORE) {
+#pragma unroll 4
+      for (int k = 0; k < 16; ++k) {
+        const int row = 16 * pw + k;
+        const v4i v = *(const lds_v4i*)(smem + row * kEpiPitch + 16 * lane);
+        const int m_r = row0 + row;
+        if (m_r < rows_valid) {
+          const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
+          store_out(v, (v4i*)(dst + rowb * kDv + 8 * lane), sg.single);
+        }
+      }
+    }
+  } else {
+    float* dst = (float*)p.part_o + (size_t)sg.slot * rows_per_b * kDv;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (!SCORE && (pw >> 2) == h) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int row = 32 * rb + ne, col = 64 * (pw & 3) + 32 * j + 8 * gq + 4 * he;
+              const v16f& acc = o[4 * j + rb];
+              *(__attribute__((address_space(3))) v4f*)(smem + row * kEpiPitch + 4 * col) =
+                  v4f{acc[4 * gq + 0] * invr[rb], acc[4 * gq + 1] * invr[rb], acc[4 * gq + 2] * invr[rb],
+                      acc[4 * gq + 3] * invr[rb]};
+            }
+          }
+        }
+      }
+      lds_barrier();
+      if constexpr (!SCORE) {
+#pragma unroll 4
+        for (int k = 0; k < 16; ++k) {
+          const int row = 16 * pw + k;
+          const v4f v = *(const __attribute__((address_space(3))) v4f*)(smem + row * kEpiPitch + 16 * lane);
+          const int m_r = row0 + row;
+          if (m_r < rows_valid) {
+            const size_t rowb = (size_t)gF * p.H + (size_t)m_r;
+            *(v4f*)(dst + rowb * kDv + 256 * h + 4 * lane) = v;
+          }
+        }
+      }
+      lds_barrier();
+    }
+  }
+}
+
+// The workgroup's slice of its row's work, segment by segment: finds the row's
+// total work T and the slice's first sequence, records the merge metadata, and
+// calls seg(sg, g, mt) for each (slice, sequence) segment in order.  Uniform
+// across the workgroup (every wave computes the same answer).
+template <int UK, bool WIN, typename SegFn>
+__device__ __forceinline__ void for_each_segment(const PartialParams& p, int tid, int lane, SegFn&& seg) {
   int w, u;
   if (p.xcd_map) {
     // slices are dealt to the 8 XCDs in turn.  Few rows: the U workgroups of one
@@ -1513,10 +2103,42 @@ mla_split_kv_partial(PartialParams p) {
       meta_u[2 * b] = w;
       meta_u[2 * b + 1] = slice_of_unit(P + nb - 1, T, p.G);
     }
-    run_segment<DT, FAST, WIN, XPV>(p, smem, s_flag, sg, g, mt, wave, lane);
+    seg(sg, g, mt);
     cur = seg_end;
     P += nb;
     ++b;
+  }
+}
+
+template <int DT, bool FAST, bool WIN, bool XPV>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mla_split_kv_partial(PartialParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kLdsBytes];
+  __shared__ int s_flag[4];
+  lds_t* smem = (lds_t*)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases in SGPRs
+  for_each_segment<Traits<DT>::kTile, WIN>(p, tid, lane, [&](const SegmentCtx& sg, int g, int mt) {
+    run_segment<DT, FAST, WIN, XPV>(p, smem, s_flag, sg, g, mt, wave, lane);
+  });
+}
+
+template <bool FAST, bool WIN>
+__global__ void __launch_bounds__(kThreadsR) __attribute__((amdgpu_waves_per_eu(3, 3)))
+mla_split_kv_fp8_roles(PartialParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[kRLdsBytes];
+  lds_t* smem = (lds_t*)smem_raw;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // two instantiations in separate branches: a wave's registers hold only its role's state
+  if (wave < 4) {
+    for_each_segment<64, WIN>(p, tid, lane, [&](const SegmentCtx& sg, int g, int mt) {
+      run_segment_roles<FAST, WIN, true>(p, smem, sg, g, mt, wave, lane);
+    });
+  } else {
+    for_each_segment<64, WIN>(p, tid, lane, [&](const SegmentCtx& sg, int g, int mt) {
+      run_segment_roles<FAST, WIN, false>(p, smem, sg, g, mt, wave, lane);
+    });
   }
 }
 
@@ -1635,6 +2257,115 @@ __global__ void __launch_bounds__(256) mla_combine(CombineParams p) {
   }
   *(uint32_t*)(p.out + orow * kDv + d) = pack_bf16x2(acc0, acc1);
   if (p.lse != nullptr && tid == 0) p.lse[orow] = lse_out;
+}
+
+// ---------------------------------------------------------------------------
+// Merge for rows spread over many slices: one wave per (output row, quarter of
+// the 512 latent dims), four waves (one row) per workgroup, no barriers.  A
+// load instruction covers 16 bytes of a lane for SPI slices at once (the
+// quarter is 16 lanes of bf16 or 32 lanes of fp32), so 16 instructions keep a
+// whole chunk of 16 SPI slices in flight (16 KiB per wave).  Each lane then sums
+// its slices' values, weighted by exp(lse_s - LSE) (broadcast from the lane
+// that computed them), and the lane groups holding the same dims combine by
+// shuffles.  Empty slices' stale bytes are selected away, never multiplied.
+// ---------------------------------------------------------------------------
+template <bool BF16P>
+__global__ void __launch_bounds__(256) mla_combine_wide(CombineParams p) {
+  constexpr int LPS = BF16P ? 16 : 32;  // lanes covering one slice's quarter row (16 bytes each)
+  constexpr int SPI = 64 / LPS;         // slices per load instruction
+  constexpr int CS = 16 * SPI;          // slices per chunk (16 loads in flight)
+  const int lane = threadIdx.x & 63;
+  const int quarter = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long long grow = (long long)blockIdx.x;
+  if (grow >= (long long)p.B * p.rows_per_b) return;
+  const int b = (int)(grow / p.rows_per_b);
+  const int row = (int)(grow - (long long)b * p.rows_per_b);
+  size_t orow;
+  if (!merge_out_row(p, b, row, orow)) return;
+  int w0, w1;
+  long long T;
+  merge_slices(p, b, row, w0, w1, T);
+  if (w0 >= w1) return;  // single slice: written by the partial kernel
+  const int n = w1 - w0 + 1;
+  auto lse_of = [&](int s) -> float {
+    if (T < p.G && slice_start(s, T, p.G) == slice_start(s + 1, T, p.G)) return -INFINITY;
+    return p.part_lse[(size_t)(s + b) * p.rows_per_b + row];
+  };
+  float mx = -INFINITY;
+  for (int i = lane; i < n; i += 64) mx = fmaxf(mx, lse_of(w0 + i));
+  mx = wave_max(mx);
+  float sum = 0.f;
+  if (mx > -INFINITY)
+    for (int i = lane; i < n; i += 64) sum += expf(lse_of(w0 + i) - mx);
+  sum = wave_sum(sum);
+  const float lse_out = mx > -INFINITY ? mx + logf(sum) : -INFINITY;
+
+  const int grp = lane / LPS, sub = lane - grp * LPS;  // this lane: slice grp of each SPI, 16 bytes sub
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  const size_t slot_elems = (size_t)p.rows_per_b * kDv;  // elements between consecutive slots
+  const size_t base = ((size_t)(w0 + b) * p.rows_per_b + row) * kDv + 128 * quarter + (BF16P ? 8 : 4) * sub;
+  if (mx > -INFINITY) {
+    for (int c0 = 0; c0 < n; c0 += CS) {
+      const int cn = min(CS, n - c0);
+      // slice weights of the chunk, one per lane (lanes past the chunk: 0)
+      const float wl = lane < cn ? expf(lse_of(w0 + c0 + lane) - lse_out) : 0.f;
+      v4i x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int sl = SPI * i + grp;  // slice of the chunk this lane loads with instruction i
+        x[i] = v4i{0, 0, 0, 0};
+        if (sl < cn) {
+          if constexpr (BF16P) {
+            x[i] = *(const v4i*)((const uint16_t*)p.part_o + base + (size_t)(c0 + sl) * slot_elems);
+          } else {
+            x[i] = *(const v4i*)((const float*)p.part_o + base + (size_t)(c0 + sl) * slot_elems);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int sl = SPI * i + grp;
+        const float wgt = __shfl(wl, sl < 64 ? sl : 0, 64);
+        const bool use = sl < cn && wgt > 0.f;
+        if constexpr (BF16P) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t u = (uint32_t)x[i][e];
+            acc[2 * e] += use ? wgt * __builtin_bit_cast(float, u << 16) : 0.f;
+            acc[2 * e + 1] += use ? wgt * __builtin_bit_cast(float, u & 0xffff0000u) : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // (through a scalar: a bit cast of the vector element itself read element 0 every time)
+            const int xe = x[i][e];
+            acc[e] += use ? wgt * __builtin_bit_cast(float, xe) : 0.f;
+          }
+        }
+      }
+    }
+  }
+  // lanes sub, sub + LPS, ... hold the same dims: sum across the lane groups
+#pragma unroll
+  for (int o2 = LPS; o2 < 64; o2 <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (BF16P || e < 4) acc[e] += __shfl_xor(acc[e], o2, 64);
+    }
+  }
+  if (lane < LPS) {
+    if constexpr (BF16P) {
+      const v4i packed = v4i{(int)pack_bf16x2(acc[0], acc[1]), (int)pack_bf16x2(acc[2], acc[3]),
+                             (int)pack_bf16x2(acc[4], acc[5]), (int)pack_bf16x2(acc[6], acc[7])};
+      *(v4i*)(p.out + orow * kDv + 128 * quarter + 8 * sub) = packed;
+    } else {
+      const v2i packed = v2i{(int)pack_bf16x2(acc[0], acc[1]), (int)pack_bf16x2(acc[2], acc[3])};
+      *(v2i*)(p.out + orow * kDv + 128 * quarter + 4 * sub) = packed;
+    }
+  }
+  if (p.lse != nullptr && quarter == 0 && lane == 0) p.lse[orow] = lse_out;
 }
 
 // ---------------------------------------------------------------------------
@@ -1784,6 +2515,12 @@ __global__ void __launch_bounds__(256) mla_kv_pack_fp8(PackParams p) {
 
 }  // namespace
 
+template <bool FAST>
+void launch_fp8_roles(const PartialParams& p, bool win, dim3 grid, hipStream_t stream) {
+  if (win) hipLaunchKernelGGL((mla_split_kv_fp8_roles<FAST, true>), grid, dim3(kThreadsR), 0, stream, p);
+  else hipLaunchKernelGGL((mla_split_kv_fp8_roles<FAST, false>), grid, dim3(kThreadsR), 0, stream, p);
+}
+
 template <int DT, bool XPV>
 void launch_partial_dt(const PartialParams& p, bool fast_pages, bool win, dim3 grid, dim3 block, hipStream_t stream) {
   if (fast_pages) {
@@ -1806,7 +2543,15 @@ hipError_t launch_partial(const PartialParams& p, int dtype, bool fast_pages, hi
   // window's per-row state costs them no registers
   const bool win = p.window > 0;
   switch (dtype) {
-    case kFp8: launch_partial_dt<kFp8, true>(p, fast_pages, win, grid, block, stream); break;
+    case kFp8:
+      if ((p.kernel == 0 ? kDefaultFp8Kernel : p.kernel) == 1) {
+        launch_partial_dt<kFp8, true>(p, fast_pages, win, grid, block, stream);  // the four-wave kernel
+      } else if (fast_pages) {
+        launch_fp8_roles<true>(p, win, grid, stream);
+      } else {
+        launch_fp8_roles<false>(p, win, grid, stream);
+      }
+      break;
     case kFp16: launch_partial_16<kFp16>(p, fast_pages, win, grid, block, stream); break;
     case kMixed: launch_partial_16<kMixed>(p, fast_pages, win, grid, block, stream); break;
     default: launch_partial_16<kBf16>(p, fast_pages, win, grid, block, stream); break;
@@ -1819,9 +2564,13 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   if (combine_per_wave(p.B, p.G)) {
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
     hipLaunchKernelGGL(mla_combine_rows, grid, block, 0, stream, p);
-  } else {
+  } else if (p.merge_kernel == 1) {
     const dim3 grid((unsigned)rows), block(256);
     hipLaunchKernelGGL(mla_combine, grid, block, 0, stream, p);
+  } else {
+    const dim3 grid((unsigned)rows), block(256);
+    if (p.part_bf16) hipLaunchKernelGGL(mla_combine_wide<true>, grid, block, 0, stream, p);
+    else hipLaunchKernelGGL(mla_combine_wide<false>, grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -61,7 +61,7 @@ def test_plan_fold_factor_and_workspace(B, q_len, H, L, F):
     if ns > 1:
         assert ns < 8 or ns % 8 == 0  # equal share per XCD once there are enough slices
         rows = q_len * H
-        need = (ns + B) * rows * (512 * 2 + 4) + U * B * 8 + U * 8  # bf16 partials; slice ranges and T per row
+        need = (ns + B) * rows * (512 * 4 + 4) + U * B * 8 + U * 8  # fp32-sized partials; slice ranges, T per row
         assert need <= ws <= need + 3 * 256
     else:
         assert ws == 0
@@ -131,17 +131,28 @@ def test_validation_errors_without_device():
 
 
 def test_options_layout_matches_header():
-    # mla_options: five int32 fields, three reserved int32, then a pointer at byte 32
+    # mla_options: seven int32 fields, one reserved int32, then a pointer at byte 32
     o = mla.MlaOptions
     assert [o.num_splits.offset, o.no_fold.offset, o.partial_fp32.offset, o.stages.offset, o.window.offset,
-            o.reserved.offset, o.split_event.offset] == [0, 4, 8, 12, 16, 20, 32]
+            o.kernel.offset, o.merge.offset, o.reserved.offset, o.split_event.offset] == [0, 4, 8, 12, 16, 20, 24,
+                                                                                         28, 32]
     assert ctypes.sizeof(o) == 40
     text = open(HEADER).read()
     body = text[text.index("typedef struct mla_options"):text.index("} mla_options;")]
     fields = re.findall(r"(int32_t|void\*)\s+(\w+)(\[\d+\])?;", body)
-    assert [f[1] for f in fields] == ["num_splits", "no_fold", "partial_fp32", "stages", "window", "reserved",
-                                      "split_event"]
-    assert re.search(r"int32_t\s+reserved\[3\];", body)
+    assert [f[1] for f in fields] == ["num_splits", "no_fold", "partial_fp32", "stages", "window", "kernel",
+                                      "merge", "reserved", "split_event"]
+    assert re.search(r"int32_t\s+reserved\[1\];", body)
+
+
+def test_kernel_and_merge_options_validated_before_any_device_work():
+    L = mla.lib()
+    shape = _shape()
+    for kw, word in ((dict(kernel=3), b"kernel"), (dict(kernel=-1), b"kernel"), (dict(merge=2), b"merge")):
+        opts = mla.options(**kw)
+        rc = L.mla_decode_ex(ctypes.byref(shape), 16, 16, 16, 16, 1.0, 1.0, 1.0, 16, 16, None, 0, None,
+                             ctypes.byref(opts))
+        assert rc == -3 and word in L.mla_last_error()
 
 
 def test_stages_option_validated_before_any_device_work():
@@ -228,3 +239,174 @@ def test_varlen_validation_without_device():
     assert call(cu=18) == -4
     assert call(total_q=0) == 0  # no new token anywhere: nothing enqueued
     assert call(q=None) == -1
+
+
+# ---------------------------------------------------------------- the binding's own checks (no device needed)
+def _cpu_inputs(B=2, q_len=4, H=8, pages=6, max_pages=3):
+    import torch
+
+    q = torch.zeros(B, q_len, H, 576, dtype=torch.float8_e4m3fn)
+    kv = torch.zeros(pages, 64, 576, dtype=torch.float8_e4m3fn)
+    bt = torch.zeros(B, max_pages, dtype=torch.int32)
+    sl = torch.full((B,), 100, dtype=torch.int32)
+    return q, kv, bt, sl
+
+
+def test_binding_rejects_batch_mismatches():
+    import torch
+
+    q, kv, bt, sl = _cpu_inputs()
+    with pytest.raises(ValueError, match="block_table"):
+        mla.decode(q, kv, bt[:1], sl, 0.1, max_seq_len=100)
+    with pytest.raises(ValueError, match="seq_lens"):
+        mla.decode(q, kv, bt, sl[:1], 0.1, max_seq_len=100)
+    with pytest.raises(ValueError, match="block_table"):
+        mla.decode(q, kv, torch.zeros(3, 3, dtype=torch.int32), torch.zeros(3, dtype=torch.int32), 0.1,
+                   max_seq_len=100)
+
+
+def test_binding_rejects_bad_outputs_and_workspace():
+    import torch
+
+    q, kv, bt, sl = _cpu_inputs()
+    good_out = torch.empty(2, 4, 8, 512, dtype=torch.bfloat16)
+    good_lse = torch.empty(2, 4, 8, dtype=torch.float32)
+    bad_outs = [torch.empty(2, 4, 8, 512, dtype=torch.float32),      # dtype
+                torch.empty(2, 4, 8, 256, dtype=torch.bfloat16),     # shape
+                torch.empty(2, 4, 512, 8, dtype=torch.bfloat16).transpose(2, 3)]  # layout
+    for o in bad_outs:
+        with pytest.raises(ValueError, match="out"):
+            mla.decode(q, kv, bt, sl, 0.1, max_seq_len=100, out=o, lse=good_lse)
+    for l in [torch.empty(2, 4, 8, dtype=torch.float64), torch.empty(2, 4, 9, dtype=torch.float32),
+              torch.empty(8, 4, 2, dtype=torch.float32).permute(2, 1, 0)]:
+        with pytest.raises(ValueError, match="lse"):
+            mla.decode(q, kv, bt, sl, 0.1, max_seq_len=100, out=good_out, lse=l)
+    with pytest.raises(ValueError, match="workspace"):
+        mla.decode(q, kv, bt, sl, 0.1, max_seq_len=100, out=good_out, lse=good_lse,
+                   workspace=torch.empty(64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="out"):
+        mla.PreparedDecode(q, kv, bt, sl, 0.1, 1.0, 1.0, max_seq_len=100, out=bad_outs[0], lse=good_lse,
+                           workspace=torch.empty(64, dtype=torch.uint8))
+
+
+def test_binding_requires_tensors_on_the_device():
+    import torch
+
+    q, kv, bt, sl = _cpu_inputs()
+    out = torch.empty(2, 4, 8, 512, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device"):
+        mla.decode(q, kv, bt, sl, 0.1, max_seq_len=100, out=out)
+    with pytest.raises(ValueError, match="device"):
+        mla.PreparedDecode(q, kv, bt, sl, 0.1, 1.0, 1.0, max_seq_len=100, out=out, lse=None,
+                           workspace=torch.empty(64, dtype=torch.uint8))
+
+
+def test_binding_varlen_checks():
+    import torch
+
+    q = torch.zeros(7, 8, 576, dtype=torch.bfloat16)
+    kv = torch.zeros(6, 64, 576, dtype=torch.bfloat16)
+    bt = torch.zeros(2, 3, dtype=torch.int32)
+    sl = torch.full((2,), 100, dtype=torch.int32)
+    cu = torch.tensor([0, 3, 7], dtype=torch.int32)
+    with pytest.raises(ValueError, match="block_table"):
+        mla.decode_varlen(q, cu, kv, bt[:1], sl, 0.1, max_q_len=4, max_seq_len=100)
+    with pytest.raises(ValueError, match="out"):
+        mla.decode_varlen(q, cu, kv, bt, sl, 0.1, max_q_len=4, max_seq_len=100,
+                          out=torch.empty(7, 8, 500, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="device"):
+        mla.decode_varlen(q, cu, kv, bt, sl, 0.1, max_q_len=4, max_seq_len=100)
+
+
+def test_binding_pack_output_checks():
+    import torch
+
+    lat = torch.zeros(4, 512, dtype=torch.bfloat16)
+    rope = torch.zeros(4, 64, dtype=torch.bfloat16)
+    for bad in [torch.empty(4, 512, dtype=torch.uint8), torch.empty(576, 4, dtype=torch.uint8).t(),
+                torch.empty(4, 576, dtype=torch.float32)]:
+        with pytest.raises(ValueError, match="out"):
+            mla.kv_pack_quantize_fp8(lat, rope, 1.0, out=bad)
+    with pytest.raises(ValueError, match="slot_mapping"):
+        mla.kv_pack_quantize_fp8(lat, rope, 1.0, out=torch.empty(8, 576, dtype=torch.uint8),
+                                 slot_mapping=torch.zeros(3, dtype=torch.int64))
+
+
+# ---------------------------------------------------------------- tensor descriptors through the C ABI
+def _desc_args(**over):
+    """Descriptors of a valid fp8 call on fake (aligned, never dereferenced) device addresses."""
+    def t(dtype, shape, stride=None, data=0x10000):
+        d = mla.MlaTensor()
+        d.data, d.dtype, d.ndim = data, dtype, len(shape)
+        if stride is None:
+            stride, acc = [], 1
+            for e in reversed(shape):
+                stride.insert(0, acc)
+                acc *= e
+        for i, (e, s) in enumerate(zip(shape, stride)):
+            d.shape[i], d.stride[i] = e, s
+        return d
+
+    a = dict(q=t(mla.ELEM_FP8_E4M3, [2, 4, 32, 576]), kv=t(mla.ELEM_FP8_E4M3, [100, 64, 576]),
+             bt=t(mla.ELEM_INT32, [2, 10]), sl=t(mla.ELEM_INT32, [2]), out=t(mla.ELEM_BF16, [2, 4, 32, 512]),
+             lse=t(mla.ELEM_FP32, [2, 4, 32]))
+    a.update({k: (t(*v) if isinstance(v, tuple) else v) for k, v in over.items()})
+    return a
+
+
+def _call_desc(a, max_seq_len=640, num_splits=0):
+    ws = mla.MlaWorkspace()
+    ws.data, ws.bytes, ws.num_splits, ws.max_seq_len = 0x20000, 1 << 30, num_splits, max_seq_len
+    L = mla.lib()
+    ref = lambda d: ctypes.byref(d) if d is not None else None
+    return L.mla_decode_tensors(ref(a["q"]), ref(a["kv"]), ref(a["bt"]), ref(a["sl"]), 1.0, 1.0, 1.0, ref(a["out"]),
+                                ref(a["lse"]), ctypes.byref(ws), None, None)
+
+
+def test_descriptor_strides_are_checked():
+    ERR_STRIDE = -9
+    # a strided q view (every other head), a padded block_table row, a transposed out, a strided seq_lens
+    assert _call_desc(_desc_args(q=(mla.ELEM_FP8_E4M3, [2, 4, 32, 576], [4 * 64 * 576, 64 * 576, 2 * 576, 1]))) \
+        == ERR_STRIDE
+    assert b"q must be packed" in mla.lib().mla_last_error()
+    assert _call_desc(_desc_args(bt=(mla.ELEM_INT32, [2, 10], [16, 1]))) == ERR_STRIDE
+    assert _call_desc(_desc_args(out=(mla.ELEM_BF16, [2, 4, 32, 512], [65536, 16384, 1, 32]))) == ERR_STRIDE
+    assert _call_desc(_desc_args(sl=(mla.ELEM_INT32, [2], [2]))) == ERR_STRIDE
+    assert _call_desc(_desc_args(kv=(mla.ELEM_FP8_E4M3, [100, 64, 576], [64 * 640, 640, 1]))) == ERR_STRIDE
+    # extents of 1 may carry any stride (torch reports such strides freely)
+    rc = _call_desc(_desc_args(q=(mla.ELEM_FP8_E4M3, [2, 1, 32, 576], [32 * 576, 12345, 576, 1]),
+                               out=(mla.ELEM_BF16, [2, 1, 32, 512], [32 * 512, 7, 512, 1]),
+                               lse=(mla.ELEM_FP32, [2, 1, 32], [32, 3, 1])))
+    assert rc not in (ERR_STRIDE, -3, -2, -1)
+
+
+def test_descriptor_types_and_extents_are_checked():
+    assert _call_desc(_desc_args(kv=(mla.ELEM_BF16, [100, 64, 576]))) == -2  # fp8 q over a bf16 cache
+    assert _call_desc(_desc_args(bt=(mla.ELEM_FP32, [2, 10]))) == -2
+    assert _call_desc(_desc_args(out=(mla.ELEM_FP32, [2, 4, 32, 512]))) == -2
+    assert _call_desc(_desc_args(q=(mla.ELEM_FP8_E4M3, [2, 4, 32, 512]))) == -3
+    assert _call_desc(_desc_args(bt=(mla.ELEM_INT32, [3, 10]))) == -3
+    assert _call_desc(_desc_args(out=(mla.ELEM_BF16, [2, 4, 16, 512]))) == -3
+    assert _call_desc(_desc_args(lse=(mla.ELEM_FP32, [2, 4]))) == -3
+    a = _desc_args()
+    a["q"] = None
+    assert _call_desc(a) == -1
+    a = _desc_args()
+    a["sl"].data = None
+    assert _call_desc(a) == -1
+    # the mixed pair and a NULL lse pass the descriptor checks (then the device is queried)
+    a = _desc_args(q=(mla.ELEM_BF16, [2, 4, 32, 576]))
+    a["lse"] = None
+    assert _call_desc(a) not in (-1, -2, -3, -9)
+    # sizes the plain entry point validates are still validated (max_seq_len > max_pages * page_size)
+    assert _call_desc(_desc_args(), max_seq_len=641) == -3
+
+
+def test_descriptor_layouts_match_header():
+    text = open(HEADER).read()
+    for name, cls in (("mla_tensor", mla.MlaTensor), ("mla_workspace", mla.MlaWorkspace)):
+        body = text[text.index(f"typedef struct {name}"):text.index(f"}} {name};")]
+        fields = re.findall(r"(int32_t|int64_t|size_t|void\*)\s+(\w+)(\[\d+\])?;", body)
+        assert [f[1] for f in fields] == [f[0] for f in cls._fields_], name
+    assert ctypes.sizeof(mla.MlaTensor) == 8 + 4 + 4 + 32 + 32
+    assert ctypes.sizeof(mla.MlaWorkspace) == 8 + 8 + 4 + 4

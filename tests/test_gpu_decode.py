@@ -53,6 +53,47 @@ def test_forced_splits(dtype, splits):
     assert_parity(x, out, lse, run_oracle(x))
 
 
+FP8_CASES = [c for c in CASES if c[3] == mi.FP8_E4M3]
+
+
+@pytest.mark.parametrize("B,q_len,H,dtype,lens,ps", FP8_CASES)
+def test_four_wave_fp8_kernel_parity(B, q_len, H, dtype, lens, ps):
+    """The four-wave E4M3 kernel, kept selectable beside the default twelve-wave one."""
+    x = mi.make_inputs(B, q_len, H, dtype, ("list", lens), page_size=ps, seed=100 + B * 7 + H + ps)
+    print(f"kernel=1 B={B} q_len={q_len} H={H} lens={lens} ps={ps}", flush=True)
+    ref = run_oracle(x)
+    out1, lse1 = run_gpu(x, opts=mla.options(kernel=1))
+    assert_parity(x, out1, lse1, ref)
+    out2, lse2 = run_gpu(x, opts=mla.options(kernel=2))
+    assert_parity(x, out2, lse2, ref)
+
+
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+@pytest.mark.parametrize("splits", [5, 64, 200])
+def test_four_wave_fp8_kernel_forced_splits(dtype, splits):
+    x = mi.make_inputs(3, 4, 32, dtype, ("list", [2500, 90, 1300]), seed=31)
+    print(f"kernel=1 splits={splits} dtype={dtype}", flush=True)
+    out, lse = run_gpu(x, opts=mla.options(num_splits=splits, kernel=1))
+    assert_parity(x, out, lse, run_oracle(x))
+
+
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+@pytest.mark.parametrize("partial_fp32", [False, True])
+def test_both_merge_kernels(dtype, partial_fp32):
+    """The wide merge (default) and the workgroup-per-row merge, on rows spread over many slices
+    (ragged, with empty slices): both within the bars, and the same up to summation order."""
+    x = mi.make_inputs(2, 2, 64, dtype, ("list", [9000, 37]), seed=77)
+    print(f"merge dtype={dtype} partial_fp32={partial_fp32}", flush=True)
+    ref = run_oracle(x)
+    res = []
+    for merge in (0, 1):
+        out, lse = run_gpu(x, opts=mla.options(num_splits=150, partial_fp32=partial_fp32, merge=merge))
+        assert_parity(x, out, lse, ref, partial_fp32=partial_fp32 or dtype != mi.FP8_E4M3)
+        res.append((out.float(), lse))
+    assert float((res[0][0] - res[1][0]).abs().max()) <= 2.0 ** -7
+    assert float((res[0][1] - res[1][1]).abs().max()) <= 1e-5
+
+
 @pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3, mi.BF16_Q_E4M3_KV])
 def test_fold_and_partial_precision_options(dtype):
     x = mi.make_inputs(2, 4, 16, dtype, ("list", [1800, 650]), seed=41)
@@ -380,19 +421,13 @@ def test_window_covering_every_key_is_bit_identical(dtype):
     assert torch.equal(base, win) and torch.equal(lse_b, lse_w)
 
 
-def test_window_full_size_agentic_sampled():
-    """The 80K-key FP8 workload with a 4096-key window: only the window's pages are read; the whole
-    output is checked for structure and one sequence against the oracle."""
+def test_window_full_size_agentic():
+    """The 80K-key FP8 workload with a 4096-key window: only the window's pages are read; every
+    sequence is compared with the oracle."""
     x = mi.workload_inputs("agentic_b4_q4_h32_fp8_80k")
     t = to_dev(x)
     out, lse = run_gpu(x, opts=mla.options(window=4096), tensors=t)
-    O = out_f64(out)
-    assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse.cpu().numpy()))
-    sub = mi.DecodeInputs(q=x.q[:1], kv_cache=x.kv_cache, block_table=x.block_table[:1], seq_lens=x.seq_lens[:1],
-                          dtype=x.dtype, q_scale=x.q_scale, kv_scale=x.kv_scale, softmax_scale=x.softmax_scale,
-                          page_size=x.page_size)
-    ref = run_oracle(sub, window=4096)
-    assert_parity(sub, out[:1], lse[:1], ref, flat=True)
+    assert_parity(x, out, lse, run_oracle(x, window=4096, num_threads=16), per_seq=True)
 
 
 # ---------------------------------------------------------------- fp16 inputs
@@ -416,18 +451,76 @@ def test_fp16_parity(B, q_len, H, lens, ps, kw):
     assert_parity(x, out, lse, run_oracle(x, window=kw.get("window", 0)))
 
 
-def test_fp16_large_score_growth_is_recomputed():
-    """Scores that grow by far more than fp16's range after the first tile force the row's
-    recomputation with the true maximum; the result must still match the oracle."""
-    x = mi.make_inputs(1, 1, 16, mi.FP16, ("list", [640]), page_size=64, seed=311)
-    kv = x.kv_cache.view(np.float16).astype(np.float32)
-    # the last page's keys get a large component along the queries' dimension 0
-    last = x.block_table[0, 9]
-    kv[last, :, 0] = 60.0
-    x.q.view(np.float16)[0, 0, :, 0] = np.float16(8.0)
-    x.kv_cache[:] = kv.astype(np.float16).view(np.uint16)
-    out, lse = run_gpu(x)
-    assert_parity(x, out, lse, run_oracle(x))
+# ---------------------------------------------------------------- a row max that outgrows its reference
+# The kernels take each row's exponentials relative to a reference fixed at the row's first tile.  When
+# a later tile's row max exceeds it by more than TAU log2 units (fp16: 15, so that P stays below 65504;
+# other dtypes 32), the 16-bit kernels and the four-wave E4M3 kernel recompute the segment from the
+# larger reference; the twelve-wave E4M3 kernel moves that row's reference at once and scales its sums
+# and accumulators by the power of two between the two references.
+TAU = {mi.FP8_E4M3: 32.0, mi.BF16: 32.0, mi.BF16_Q_E4M3_KV: 32.0, mi.FP16: 15.0}
+
+
+def _decode_values(codes, fmt, scale):
+    t = torch.from_numpy(codes.view(np.int16) if fmt != mi.FP8_E4M3 else codes)
+    t = t.view({mi.BF16: torch.bfloat16, mi.FP16: torch.float16}.get(fmt, torch.float8_e4m3fn))
+    return t.float().numpy().astype(np.float64) * scale
+
+
+def _encode_values(v, fmt, scale):
+    t = torch.from_numpy(np.ascontiguousarray(v / scale, dtype=np.float32))
+    if fmt == mi.FP8_E4M3:
+        assert float(t.abs().max()) <= 448.0
+        return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return t.to(torch.bfloat16 if fmt == mi.BF16 else torch.float16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _late_outlier_inputs(dtype):
+    """Two sequences whose queries share a direction, with a few keys far along it placed several
+    tiles in (two of them past the causal limit of the first tokens): every row's max score grows by
+    ~45-60 log2 units after its first tile."""
+    lens = [512, 700]
+    x = mi.make_inputs(2, 4, 32, dtype, ("list", lens), page_size=64, seed=331 + dtype)
+    qf, kf = mi.q_format(dtype), mi.kv_format(dtype)
+    rng = np.random.default_rng(17)
+    q = _decode_values(x.q, qf, x.q_scale)
+    base = rng.standard_normal((2, 576))
+    q = 0.5 * q + 2.0 * base[:, None, None, :]
+    if qf == mi.FP8_E4M3:
+        x.q_scale = float(np.abs(q).max()) / 448.0
+    x.q = _encode_values(q, qf, x.q_scale)
+    planted = {0: [(200, 1.25), (260, 1.35), (333, 1.45), (450, 1.40)],
+               1: [(300, 1.30), (640, 1.45), (698, 1.50), (699, 1.47)]}
+    for b, keys in planted.items():
+        for j, g in keys:
+            row = g * np.sign(base[b]) + 0.5 * rng.standard_normal(576)  # their V parts differ
+            row[:512] *= 0.4  # V stays O(1): the output's absolute error scales with |V|
+            x.kv_cache[x.block_table[b, j // 64], j % 64] = _encode_values(row, kf, x.kv_scale)
+    return x
+
+
+@pytest.mark.parametrize("dtype,kernel", [(mi.FP8_E4M3, 2), (mi.FP8_E4M3, 1), (mi.BF16, 0),
+                                          (mi.BF16_Q_E4M3_KV, 0), (mi.FP16, 0)])
+def test_late_large_scores_move_the_reference(dtype, kernel):
+    x = _late_outlier_inputs(dtype)
+    # Worked out on the host: with one slice per sequence, each row's reference comes from its first
+    # tile (keys 0..63 or 0..31, a subset of 0..63), and a later key exceeds it by more than TAU + 8.
+    qv = _decode_values(x.q, mi.q_format(dtype), x.q_scale)
+    kvv = _decode_values(x.kv_cache, mi.kv_format(dtype), x.kv_scale)
+    for b in range(x.B):
+        L = int(x.seq_lens[b])
+        keys = kvv[x.block_table[b, np.arange(L) // 64], np.arange(L) % 64]
+        s2 = np.einsum("thd,jd->thj", qv[b], keys) * x.softmax_scale / np.log(2.0)
+        for t in range(x.q_len):
+            n_t = L - x.q_len + t + 1
+            gap = s2[t, :, :n_t].max(axis=-1) - s2[t, :, :64].max(axis=-1)
+            assert gap.min() > TAU[dtype] + 8, (b, t, float(gap.min()))
+    print(f"dtype={dtype}: every row's max grows past its first tile's by > {TAU[dtype] + 8} log2 units", flush=True)
+    out, lse = run_gpu(x, opts=mla.options(num_splits=1, kernel=kernel))
+    ref = run_oracle(x)
+    assert_parity(x, out, lse, ref)
+    # the result mixes several planted keys rather than copying the largest one
+    top = kvv[x.block_table[0, 333 // 64], 333 % 64, :512]
+    assert float(np.abs(ref[0][0, 0, 0] - top).max()) > 2e-2
 
 
 # ---------------------------------------------------------------- bf16 q over an E4M3 cache

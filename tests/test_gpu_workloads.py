@@ -1,11 +1,10 @@
-"""Parity on the five benchmark workloads at full size, in the launch configuration
+"""Parity on the benchmark workloads at full size, in the launch configuration
 bench.py times (default plan: planned split count, folded queries, bf16 partials).
 
-The whole output is checked for the properties that hold at any size (finite,
-rows without visible keys exactly zero with LSE = -inf); a few whole sequences
-per workload (every query token and head) are recomputed by the fp64 oracle and
-compared element by element against the flat bars: bf16 O max-abs <= 1e-2, FP8 O
-<= 5e-2, LSE <= 1e-3, plus the derived per-element bound.
+Every output element of every workload -- every sequence, query token and head
+-- is compared with the fp64 oracle run on the same bytes (16 threads), against
+the flat bars (bf16 O max-abs <= 1e-2, FP8 O <= 5e-2, LSE <= 1e-3) and the
+derived per-element bound.  The largest errors of each sequence are printed.
 """
 import dataclasses
 import time
@@ -17,23 +16,11 @@ import torch
 import mla_inputs as mi
 import mla_paged_kv_decode_amd as mla
 import oracle
-from tests.gpu_util import assert_parity, out_f64, to_dev
+from tests.gpu_util import assert_parity, out_f64, to_dev, _torch_dtype
 
 pytestmark = pytest.mark.gpu
 
-
-def _sample(name, lens):
-    """Sequences recomputed by the oracle: the shortest, plus the longest or a seeded pick."""
-    order = np.argsort(lens, kind="stable")
-    picks = {int(order[0])}
-    if name.startswith("agentic"):
-        picks = {0}
-    elif name.startswith("dsv3"):
-        picks.add(int(order[len(order) // 4]))  # lengths up to 64K with q_len=1: keep the oracle to seconds
-    elif name.startswith("spec"):
-        picks.add(int(order[-1]))
-        picks.add(int(np.random.default_rng(7).integers(len(lens))))
-    return sorted(picks)
+ORACLE_THREADS = 16
 
 
 @pytest.mark.parametrize("name", list(mi.WORKLOADS))
@@ -47,32 +34,24 @@ def test_workload_parity(name):
     torch.cuda.synchronize()
     O = out_f64(out)
     L = lse.cpu().numpy().astype(np.float64)
-    assert np.all(np.isfinite(O)), "non-finite output"
-    assert not np.isnan(L).any()
+    del q, kv, out, lse
     # a token t of sequence b sees min(L_b - q_len + t + 1, L_b) keys; none -> zero row, LSE = -inf
     vis = np.minimum(x.seq_lens[:, None] - x.q_len + np.arange(x.q_len)[None, :] + 1, x.seq_lens[:, None])
     empty = vis <= 0
     assert np.array_equal(np.isneginf(L).all(axis=-1), empty)
-    assert np.all(O[empty] == 0)
 
-    for b in _sample(name, x.seq_lens):
-        t1 = time.time()
-        sub = dataclasses.replace(x, q=x.q[b:b + 1], block_table=x.block_table[b:b + 1],
-                                  seq_lens=x.seq_lens[b:b + 1])
-        ref = oracle.mla_decode(sub.q, sub.kv_cache, sub.block_table, sub.seq_lens, dtype=x.dtype,
-                                softmax_scale=x.softmax_scale, q_scale=x.q_scale, kv_scale=x.kv_scale,
-                                want_absv=True, num_threads=16)
-        print(f"    sequence {b} (L={int(x.seq_lens[b])}): oracle {time.time() - t1:.1f} s", flush=True)
-
-        assert_parity(sub, torch.from_numpy(O[b:b + 1]), torch.from_numpy(L[b:b + 1]), ref, flat=True)
+    t1 = time.time()
+    ref = oracle.mla_decode(x.q, x.kv_cache, x.block_table, x.seq_lens, dtype=x.dtype,
+                            softmax_scale=x.softmax_scale, q_scale=x.q_scale, kv_scale=x.kv_scale,
+                            want_absv=True, num_threads=ORACLE_THREADS)
+    print(f"    oracle over all {x.B} sequences: {time.time() - t1:.1f} s", flush=True)
+    assert_parity(x, torch.from_numpy(O), torch.from_numpy(L), ref, per_seq=True)
 
 
 @pytest.mark.parametrize("name", list(mi.RAGGED_PREFILL))
 def test_ragged_prefill_workload(name):
-    """The ragged prefill workloads bench.py times, at full size through mla_decode_varlen: the
-    whole output is finite, and the sequence with the fewest new tokens (every one of its
-    tokens and heads) matches the fp64 oracle."""
-    from tests.gpu_util import _torch_dtype
+    """The ragged prefill workloads bench.py times, at full size through mla_decode_varlen: every
+    sequence (every one of its new tokens and heads) against the fp64 oracle run on that sequence."""
     x, new = mi.ragged_prefill_inputs(name)
     qf = mi.q_format(x.dtype)
     q_pack = np.ascontiguousarray(np.concatenate([x.q[b, :n] for b, n in enumerate(new)], axis=0))
@@ -84,16 +63,16 @@ def test_ragged_prefill_workload(name):
                                  max_seq_len=x.max_seq_len)
     torch.cuda.synchronize()
     O = out_f64(out)
-    assert np.all(np.isfinite(O)) and np.all(np.isfinite(lse.cpu().numpy()))
-    b = int(np.argmin(new))
-    t1 = time.time()
-    sub = dataclasses.replace(x, q=np.ascontiguousarray(x.q[b:b + 1, :new[b]]), block_table=x.block_table[b:b + 1],
-                              seq_lens=x.seq_lens[b:b + 1])
-    ref = oracle.mla_decode(sub.q, sub.kv_cache, sub.block_table, sub.seq_lens, dtype=x.dtype,
-                            softmax_scale=x.softmax_scale, q_scale=x.q_scale, kv_scale=x.kv_scale, want_absv=True,
-                            num_threads=16)
-    print(f"    {name}: sequence {b} ({new[b]} new tokens, L={int(x.seq_lens[b])}): oracle {time.time() - t1:.1f} s",
-          flush=True)
-    r0 = int(np.sum(new[:b]))
-    assert_parity(sub, torch.from_numpy(O[r0:r0 + new[b]][None]), lse[r0:r0 + new[b]][None].cpu(),
-                  ref, flat=True)
+    Lg = lse.cpu().numpy().astype(np.float64)
+    for b in range(len(new)):
+        t1 = time.time()
+        sub = dataclasses.replace(x, q=np.ascontiguousarray(x.q[b:b + 1, :new[b]]),
+                                  block_table=x.block_table[b:b + 1], seq_lens=x.seq_lens[b:b + 1])
+        ref = oracle.mla_decode(sub.q, sub.kv_cache, sub.block_table, sub.seq_lens, dtype=x.dtype,
+                                softmax_scale=x.softmax_scale, q_scale=x.q_scale, kv_scale=x.kv_scale,
+                                want_absv=True, num_threads=ORACLE_THREADS)
+        print(f"    {name}: sequence {b} ({new[b]} new tokens, L={int(x.seq_lens[b])}): oracle "
+              f"{time.time() - t1:.1f} s", flush=True)
+        r0 = int(np.sum(new[:b]))
+        assert_parity(sub, torch.from_numpy(O[r0:r0 + new[b]][None]), torch.from_numpy(Lg[r0:r0 + new[b]][None]),
+                      ref)
