@@ -1303,7 +1303,11 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         if (wave_active) pv(block_base(nblocks - 1), pp0, pp1, false, 0, false);
               }
       }
-      // did any row of the workgroup outgrow its reference?
+      // did any row of the workgroup outgrow its reference?  Segments of at most 128 keys are also
+      // redone when any row's max came after its first tile: a row with few keys gives most of its
+      // weight to a handful of them, and with the row max as reference the largest p is exactly 1
+      // (E4M3: a power of two), so only the smaller weights carry the rounding of P.
+      if (attempt == 0 && ntiles * TILE <= 128) ovf = ovf || (m_seen > m_ref);
       const bool wave_ovf = __builtin_amdgcn_ballot_w64(ovf) != 0;
       if (lane == 0) s_flag[wave] = wave_ovf ? 1 : 0;
       lds_barrier();
@@ -1580,7 +1584,7 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
   v8i qreg[SCORE ? 9 : 1];  // score waves: Q of the row block (B operand, K-steps of 64)
   v16f o[SCORE ? 1 : 8];     // PV waves: o[4 j + rb] = dims 64 pw + 32 j .. + 31 of row block rb
   float m_ref = -INFINITY;
-  float l_acc = 0.f, l_acc_r = 0.f;
+  float l_acc = 0.f;
   if constexpr (!SCORE) {
     // zeros made here (opaque): a hoisted constant block would be kept, or spilled, across segments
     float z = 0.f;
@@ -1714,6 +1718,9 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
       // ---------------- score role ----------------
       v16f s0, s1;
       int pa[4], pb[4];
+      // second term of P: the E4M3 rounding residual of every element, as E2M1 codes of half
+      // its value (nibble k = K-slot k of the E4M3 operand: la = keys of s0, lb = keys of s1)
+      int la[2], lb[2];
       int sc_code = 127;
       float resc = 1.f;  // this tile's reference change of the row (1: none)
       auto qk = [&](const lds_t* st) {
@@ -1768,15 +1775,19 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
           resc = __builtin_amdgcn_exp2f(m_ref - rm);
           m_ref = rm;
           l_acc *= resc;
-          l_acc_r *= resc;
         }
         const float mref = m_ref > -INFINITY ? m_ref : 0.f;
         int e = 0;
         if (rm > -INFINITY) e = 8 - (int)ceilf(rm - mref);
         e = min(max(e, -120), 120);
         const float off = mref - (float)e;
-        float lsum = 0.f, lsum_r = 0.f;
-        auto four = [&](const v16f& sv, int w2) -> int {
+        float lsum = 0.f;
+        // Four probabilities: the E4M3 codes (returned) and the E2M1 codes of their residuals, written
+        // into bytes 2 (w2 & 1) and 2 (w2 & 1) + 1 of `lo`.  Every p is at most 256 here, so a
+        // residual is at most 8 (half an E4M3 step in [128, 256]) and half of it fits E2M1's range;
+        // with the second term each p is off by at most 2^-7 of its own binade.  O is normalised by
+        // the exact sum: the two terms differ from it by less than that.
+        auto four = [&](const v16f& sv, int w2, int& lo) -> int {
           const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * w2 + 0], p.s_scale_log2, -off));
           const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * w2 + 1], p.s_scale_log2, -off));
           const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * w2 + 2], p.s_scale_log2, -off));
@@ -1786,19 +1797,34 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
           lsum += (e0 + e1) + (e2 + e3);
           const v2f r0 = __builtin_amdgcn_cvt_pk_f32_fp8(wv, false);
           const v2f r1 = __builtin_amdgcn_cvt_pk_f32_fp8(wv, true);
-          lsum_r += (r0[0] + r0[1]) + (r1[0] + r1[1]);
+          // (the conversion divides by its scale: codes of d / 2)
+          uint32_t lw = (uint32_t)lo;
+          if ((w2 & 1) == 0) {  // (byte selects must be literal constants)
+            lw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lw, e0 - r0[0], e1 - r0[1], 2.f, 0);
+            lw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lw, e2 - r1[0], e3 - r1[1], 2.f, 1);
+          } else {
+            lw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lw, e0 - r0[0], e1 - r0[1], 2.f, 2);
+            lw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lw, e2 - r1[0], e3 - r1[1], 2.f, 3);
+          }
+          lo = (int)lw;
           return wv;
         };
+        la[0] = la[1] = lb[0] = lb[1] = 0;
 #pragma unroll
         for (int w2 = 0; w2 < 4; ++w2) {
-          pa[w2] = four(s0, w2);
-          pb[w2] = four(s1, w2);
+          pa[w2] = four(s0, w2, la[w2 >> 1]);
+          pb[w2] = four(s1, w2, lb[w2 >> 1]);
         }
         l_acc += __builtin_ldexpf(lsum, -e);
-        l_acc_r += __builtin_ldexpf(lsum_r, -e);
         sc_code = 127 - e;
       };
-      auto publish = [&]() {
+      // The second term of P(t) goes into the rope columns of tile t's own stage (bytes 512..575 of
+      // its 64 rows): the score waves are done with them once the barrier after the scores has
+      // passed, and the stage is not reloaded before the PV of tile t has read them.  Entry
+      // 64 rb + lane (16 bytes) sits at row entry / 4, bytes 512 + 16 (entry % 4).
+      auto lo_entry = [&](const lds_t* st, int e) -> const lds_t* { return st + (e >> 2) * RB + 512 + 16 * (e & 3); };
+      auto publish = [&](int t) {
+        *(lds_v4i*)lo_entry(stage(t), 64 * sr + lane) = v4i{la[0], la[1], lb[0], lb[1]};
         *(lds_v4i*)(smem + kRP + 2048 * sr + 16 * lane) = v4i{pa[0], pa[1], pa[2], pa[3]};
         *(lds_v4i*)(smem + kRP + 2048 * sr + 1024 + 16 * lane) = v4i{pb[0], pb[1], pb[2], pb[3]};
         *(lds_i32*)(smem + kRScale + 256 * sr + 4 * lane) = sc_code;
@@ -1851,9 +1877,18 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
           const v4i x = *(const lds_v4i*)(smem + kRP + 2048 * rb + pa_);
           const v4i y = *(const lds_v4i*)(smem + kRP + 2048 * rb + 1024 + pa_);
           const int scb = *(const lds_i32*)(smem + kRScale + 256 * rb + (pa_ >> 2));
+          // The E2M1 operand of a column: lane half h takes bytes 8h..8h+7 of the entries of lanes
+          // n and n + 32 (its K-slots are those of E4M3 bytes 16h..16h+15 of both lane halves).
+          const int hb = 8 * (lane >> 5), ln = lane & 31;
+          const v2i l0 = *(const lds_v2i*)(lo_entry(st, 64 * rb + ln) + hb);
+          const v2i l1 = *(const lds_v2i*)(lo_entry(st, 64 * rb + 32 + ln) + hb);
           const v8i pr = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+          const v8i pl = v8i{l0[0], l0[1], l1[0], l1[1], 0, 0, 0, 0};
           o[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v0, pr, o[rb], 0, 0, 0, 127, 0, scb);
           o[4 + rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v1, pr, o[4 + rb], 0, 0, 0, 127, 0, scb);
+          // the residual term: B in E2M1 (blgp 4), twice the E4M3 term's scale
+          o[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v0, pl, o[rb], 0, 4, 0, 127, 0, scb + 1);
+          o[4 + rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v1, pl, o[4 + rb], 0, 4, 0, 127, 0, scb + 1);
           // the MFMAs stay here (left alone, the compiler sinks them past the barrier that
           // follows, keeping every P operand live across it)
           asm volatile("" : "+v"(o[rb]), "+v"(o[4 + rb]));
@@ -1902,7 +1937,7 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
       issue_tile(3);
       if constexpr (SCORE) score_tile(0);
       lds_barrier();
-      if constexpr (SCORE) publish();
+      if constexpr (SCORE) publish(0);
       wait_next();  // P(0) visible, tile 1 landed
 
       for (int t = 1; t < ntiles; ++t) {
@@ -1913,7 +1948,7 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
           pv_tile(t - 1);
         }
         lds_barrier();  // PV of tile t-1 is done: the P buffer and the stage of tile t-1 are free
-        if constexpr (SCORE) publish();
+        if constexpr (SCORE) publish(t);
         issue_tile(t + 3);
         wait_next();  // P(t) visible, tile t+1 landed
       }
@@ -1935,9 +1970,8 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
   const int row0 = mt * kTileM;
   if constexpr (SCORE) {
     const float l_tot = xor32_sum(l_acc);
-    const float l_r = xor32_sum(l_acc_r);
-    const bool has = l_tot > 0.f && l_r > 0.f;
-    const float inv = has ? p.v_scale / l_r : 0.f;
+    const bool has = l_tot > 0.f;
+    const float inv = has ? p.v_scale / l_tot : 0.f;
     const float lse_v = has ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
     if (he == 0) s_inv[32 * sr + ne] = inv;
     const int m_l = row0 + 32 * sr + ne;

@@ -13,6 +13,17 @@ import oracle
 BF16_O_TOL = 1e-2
 FP8_O_TOL = 5e-2
 LSE_TOL = 1e-3
+# The output is bf16: the exact result rounded to bf16 is already off by up to half an ulp of
+# the value (2^-8 |O| at most), which alone passes 1e-2 once |O| > 2.56 (few-key rows of N(0,1)
+# values reach |O| ~ 4).  The flat bar therefore applies to the error beyond that rounding:
+# |dO| <= bar + half_ulp_bf16(O_ref), element by element.
+
+
+def half_ulp_bf16(x):
+    """Half the spacing of bf16 values at |x| (8 significant bits), 0 at 0."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.ldexp(1.0, (e - 8).astype(np.int64)), 0.0)
 # Element-wise bound derived from the arithmetic (any input).  The softmax weights are
 # rounded to the PV operand format before the MFMA: unit roundoff u_P = 2^-8 for bf16
 # (8-bit significand), 2^-11 for fp16 (11-bit), 2^-4 for E4M3 (4-bit significand; the
@@ -71,7 +82,8 @@ def assert_parity(x, out, lse, ref, rows=None, partial_fp32=False, per_seq=False
     """Element-wise parity with the oracle, on every element compared.
 
     Rows with no visible key are exact zeros / -inf; LSE within 1e-3; |dO|
-    within the flat bar of the dtype (FP8 cache 5e-2, bf16 / fp16 1e-2) and
+    within the flat bar of the dtype (FP8 cache 5e-2, bf16 / fp16 1e-2) plus
+    half a bf16 ulp of the exact value (the output's own rounding), and
     within the derived per-element bound.  per_seq=True also prints the
     largest errors of every sequence (axis 0).
     """
@@ -94,8 +106,9 @@ def assert_parity(x, out, lse, ref, rows=None, partial_fp32=False, per_seq=False
     fin = ~empty
     l_err = float(np.max(np.abs(L[fin] - lse_ref[fin]))) if fin.any() else 0.0
     worst = float((err / bound).max()) if err.size else 0.0
-    print(f"    max|dO|={o_err:.3e} max|dLSE|={l_err:.3e} worst dO/bound={worst:.3f} "
-          f"(bars: O {o_tol(x.dtype):.0e}, LSE {LSE_TOL:.0e})", flush=True)
+    over = float((err - half_ulp_bf16(O_ref)).max()) if err.size else 0.0  # beyond the output rounding
+    print(f"    max|dO|={o_err:.3e} (beyond bf16 rounding of the result: {over:.3e}) max|dLSE|={l_err:.3e} "
+          f"worst dO/bound={worst:.3f} (bars: O {o_tol(x.dtype):.0e}, LSE {LSE_TOL:.0e})", flush=True)
     if per_seq and err.size:
         dl = np.where(fin, np.abs(L - np.where(fin, lse_ref, 0.0)), 0.0)
         eo = err.reshape(err.shape[0], -1).max(axis=1)
@@ -104,5 +117,6 @@ def assert_parity(x, out, lse, ref, rows=None, partial_fp32=False, per_seq=False
               " ".join(f"{i}:{a:.2e}/{b:.1e}" for i, (a, b) in enumerate(zip(eo, el))), flush=True)
     assert l_err <= LSE_TOL, f"max|dLSE| = {l_err}"
     assert worst <= 1.0, f"|dO| exceeds the derived bound by {worst:.3f}x (max|dO| = {o_err})"
-    assert o_err <= o_tol(x.dtype), f"max|dO| = {o_err} above the flat bar {o_tol(x.dtype)}"
+    assert over <= o_tol(x.dtype), (f"max|dO| beyond the bf16 rounding of the result = {over} above the flat bar "
+                                    f"{o_tol(x.dtype)} (max|dO| = {o_err})")
     return o_err, l_err

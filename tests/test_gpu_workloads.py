@@ -3,8 +3,8 @@ bench.py times (default plan: planned split count, folded queries, bf16 partials
 
 Every output element of every workload -- every sequence, query token and head
 -- is compared with the fp64 oracle run on the same bytes (16 threads), against
-the flat bars (bf16 O max-abs <= 1e-2, FP8 O <= 5e-2, LSE <= 1e-3) and the
-derived per-element bound.  The largest errors of each sequence are printed.
+the flat bars (bf16 O max-abs <= 1e-2, FP8 O <= 5e-2, each on top of the
+bf16 rounding of the result; LSE <= 1e-3) and the derived per-element bound.  The largest errors of each sequence are printed.
 """
 import dataclasses
 import time
