@@ -266,6 +266,24 @@ int mla_decode_tensors(const mla_tensor* q, const mla_tensor* kv_cache, const ml
                        const mla_tensor* out, const mla_tensor* lse, const mla_workspace* workspace, void* stream,
                        const mla_options* options);
 
+/*
+ * mla_decode_ex without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The workspace is a file-scope device
+ * array of 160 MiB inside the library (one copy per GPU, held until the process
+ * ends; its address is looked up once per device, on that device's first call).
+ * The call allocates and frees nothing.  Inputs, outputs, sizes, options and
+ * errors are those of mla_decode_ex; in addition, a shape whose plan needs
+ * more than 160 MiB (mla_workspace_bytes_ex) fails with MLA_ERR_WORKSPACE
+ * before anything is enqueued.  The array needs no clearing: nothing in it
+ * carries over from one call to the next.  Every call on one GPU uses the
+ * same array, so calls that overlap on one GPU (concurrent streams, or
+ * threads) race on it; calls on one stream are ordered and safe.
+ */
+int mla_decode_static(const mla_shape* shape, const void* q, const void* kv_cache, const int32_t* block_table,
+                      const int32_t* seq_lens, float softmax_scale, float q_scale, float kv_scale, void* out,
+                      float* lse, void* stream, const mla_options* options);
+
 /* Workspace size and split count for mla_decode_ex with `options` (NULL = defaults). */
 int mla_workspace_bytes_ex(int32_t batch, int32_t q_len, int32_t num_heads, int32_t max_seq_len,
                            const mla_options* options, int32_t* num_splits, size_t* workspace_bytes);

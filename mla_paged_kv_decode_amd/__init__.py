@@ -36,7 +36,7 @@ ELEM_BF16, ELEM_FP8_E4M3, ELEM_FP16, ELEM_FP32, ELEM_INT32 = 1, 2, 3, 4, 5
 
 # every symbol include/mla_decode.h declares
 EXPORTS = ["mla_get_split_kv_and_workspace", "mla_decode", "mla_decode_ex", "mla_decode_varlen",
-           "mla_decode_tensors", "mla_workspace_bytes_ex", "mla_plan_for_cus", "mla_kv_pack_quantize_fp8",
+           "mla_decode_tensors", "mla_decode_static", "mla_workspace_bytes_ex", "mla_plan_for_cus", "mla_kv_pack_quantize_fp8",
            "mla_last_error", "mla_version"]
 
 
@@ -113,6 +113,8 @@ def lib():
                                     ctypes.POINTER(MlaOptions)]
     L.mla_kv_pack_quantize_fp8.argtypes = [p, ctypes.c_int64, p, ctypes.c_int64, p, i32, ctypes.c_float, p,
                                            ctypes.c_int64, p]
+    L.mla_decode_static.argtypes = [ctypes.POINTER(MlaShape), p, p, p, p, fl, fl, fl, p, p, p,
+                                    ctypes.POINTER(MlaOptions)]
     tp = ctypes.POINTER(MlaTensor)
     L.mla_decode_tensors.argtypes = [tp, tp, tp, tp, fl, fl, fl, tp, tp, ctypes.POINTER(MlaWorkspace), p,
                                      ctypes.POINTER(MlaOptions)]
@@ -120,7 +122,7 @@ def lib():
     L.mla_last_error.argtypes = []
     L.mla_version.restype = ctypes.c_int
     for f in ("mla_get_split_kv_and_workspace", "mla_workspace_bytes_ex", "mla_plan_for_cus", "mla_decode",
-              "mla_decode_ex", "mla_decode_varlen", "mla_decode_tensors",
+              "mla_decode_ex", "mla_decode_varlen", "mla_decode_tensors", "mla_decode_static",
               "mla_kv_pack_quantize_fp8"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
@@ -338,6 +340,29 @@ class PreparedDecode:
         rc = self._fn(*self._args)
         if rc != 0:
             _check(rc)
+
+
+def decode_static(q, kv_cache, block_table, seq_lens, softmax_scale: float, q_scale: float = 1.0,
+                  kv_scale: float = 1.0, *, max_seq_len: int, out, lse=None, opts: MlaOptions | None = None,
+                  stream=None):
+    """mla_decode_static: the decode with the library's own static workspace (no allocation in the call).
+    out (and lse, if given) are caller-owned."""
+    torch = _torch()
+    _check_layout(q, kv_cache, block_table, seq_lens)
+    B, q_len, H = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    if out is None:
+        raise ValueError("pass `out`: the static entry point writes into caller-owned outputs")
+    _check_outputs(q, out, lse, None, (B, q_len, H, D_V), (B, q_len, H))
+    _check_device(q, ("kv_cache", kv_cache), ("block_table", block_table), ("seq_lens", seq_lens), ("out", out),
+                  ("lse", lse))
+    shape = make_shape(q, kv_cache, block_table, max_seq_len)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib().mla_decode_static(ctypes.byref(shape), q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
+                                   seq_lens.data_ptr(), float(softmax_scale), float(q_scale), float(kv_scale),
+                                   out.data_ptr(), lse.data_ptr() if lse is not None else None, stream,
+                                   ctypes.byref(opts) if opts is not None else None))
+    return out, lse
 
 
 def tensor_desc(t) -> MlaTensor:

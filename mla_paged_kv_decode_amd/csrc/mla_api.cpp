@@ -181,7 +181,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t* bt, const int32_t* seq_lens,
                 float softmax_scale, float q_scale, float kv_scale, void* out, float* lse, void* ws, size_t ws_bytes,
                 void* stream, const mla_options* opt,
-                const int32_t* cu_q = nullptr, int32_t total_q = 0) {
+                const int32_t* cu_q = nullptr, int32_t total_q = 0, bool static_ws = false) {
   if (opt && (opt->stages < 0 || opt->stages > 2)) return fail(MLA_ERR_SHAPE, "options.stages must be 0, 1 or 2");
   if (opt && opt->window < 0) return fail(MLA_ERR_SHAPE, "options.window must be >= 0 (got %d)", opt->window);
   if (opt && (opt->kernel < 0 || opt->kernel > 2)) return fail(MLA_ERR_SHAPE, "options.kernel must be 0, 1 or 2");
@@ -224,6 +224,15 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
   if (rc) return rc;
   Plan pl;
   cached_plan(dev, cus, s->batch, s->q_len, s->num_heads, s->max_seq_len, opt, &pl);
+  if (static_ws) {
+    if (pl.bytes > mla::kStaticScratchBytes)
+      return fail(MLA_ERR_WORKSPACE,
+                  "this shape needs a %zu-byte workspace, more than the %zu-byte static scratch of mla_decode_static",
+                  pl.bytes, mla::kStaticScratchBytes);
+    hipError_t e = mla::static_scratch(&ws);
+    if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    ws_bytes = mla::kStaticScratchBytes;
+  }
   if (pl.bytes > 0) {
     if (!ws) return fail(MLA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", pl.bytes);
     if (!aligned(ws, kAlign)) return fail(MLA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -402,6 +411,13 @@ int mla_kv_pack_quantize_fp8(const void* latent, int64_t latent_stride, const vo
   hipError_t e = mla::launch_pack_fp8(p, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "pack kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int mla_decode_static(const mla_shape* shape, const void* q, const void* kv_cache, const int32_t* block_table,
+                      const int32_t* seq_lens, float softmax_scale, float q_scale, float kv_scale, void* out,
+                      float* lse, void* stream, const mla_options* options) {
+  return decode_impl(shape, q, kv_cache, block_table, seq_lens, softmax_scale, q_scale, kv_scale, out, lse, nullptr, 0,
+                     stream, options, nullptr, 0, true);
 }
 
 // Tensor-descriptor form: every descriptor is checked against the layout the

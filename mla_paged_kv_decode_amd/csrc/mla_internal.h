@@ -84,6 +84,12 @@ inline bool combine_per_wave(int B, int G) { return (long long)G < 16LL * B; }
 // would do all of PV.  With every row block filled the own-rows layout is faster.
 inline bool cross_wave_pv(int H_eff) { return H_eff < 128; }
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+// mla_decode_static's workspace: a file-scope device array of this many bytes
+// (enough for the plans of every decode workload benchmarked here, the largest
+// being 128.3 MiB); static_scratch() returns the current device's copy, looked
+// up once per device with that device current.
+constexpr size_t kStaticScratchBytes = size_t(160) << 20;
+hipError_t static_scratch(void** ptr);
 hipError_t launch_pack_fp8(const PackParams& p, hipStream_t stream);
 
 }  // namespace mla

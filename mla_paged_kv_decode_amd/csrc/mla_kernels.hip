@@ -22,9 +22,17 @@
 //    page, fused K/V pack + FP8 quantisation).
 #include <math.h>
 
+#include <map>
+#include <mutex>
 #include <type_traits>
 
 #include "mla_internal.h"
+
+// Workspace of mla_decode_static (callers that cannot allocate): one copy per
+// GPU, held until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it only stands in for the symbol); it uses the
+// device address that static_scratch() looks up per device.
+static __device__ __align__(256) uint8_t scratch[mla::kStaticScratchBytes];
 
 namespace mla {
 namespace {
@@ -2607,6 +2615,24 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
     else hipLaunchKernelGGL(mla_combine_wide<false>, grid, block, 0, stream, p);
   }
   return hipGetLastError();
+}
+
+hipError_t static_scratch(void** ptr) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;  // device -> address of that device's copy of `scratch`
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with `dev` current: its own copy
+    if (e != hipSuccess) return e;
+    it = addr.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return hipSuccess;
 }
 
 hipError_t launch_pack_fp8(const PackParams& p, hipStream_t stream) {
