@@ -1511,22 +1511,29 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
 //     then the softmax; their Q block lives in 72 VGPRs.  Each owns its rows'
 //     softmax state: a reference m_ref fixed at the row's first visible tile,
 //     P scaled per tile so its largest value lands in (128, 256], the scale
-//     2^-e handed to the PV MFMA as its E8M0 block scale, the row sums (exact,
-//     for the LSE; over the rounded P, to normalise O).
+//     2^-e handed to the PV MFMA as its E8M0 block scale, the exact row sums.
+//     P goes out in two terms: E4M3 codes, and E2M1 codes of their rounding
+//     residuals (used for sequences of at most kLoKeys keys).
 //   PV waves 4-11: O^T for latent dims [64 pw, 64 pw + 64), pw = wave - 4, and
-//     all 128 rows: 8 MFMAs (2 dim blocks x 4 row blocks) per tile, their output
-//     block in 128 VGPRs; waves 4-7 also issue the tile loads.
-// Per tile t, phase A: the score waves run the scores and softmax of tile t (at
-// raised priority while their MFMAs issue), the PV waves the PV of tile t-1, so
-// the score waves' softmax overlaps the PV MFMAs on every SIMD.  [barrier]
-// Phase B: the score waves publish P(t), its scales and the rows' rescale
-// factors; the stage of tile t-1 is reissued for tile t+3.  [barrier, tile t+1
-// landed]  Three tiles stay in flight.  A row whose max outgrows its reference
+//     all 128 rows: 8 MFMAs (2 dim blocks x 4 row blocks) per tile, 8 more for
+//     the second P term, their output block in 128 VGPRs; waves 4-7 also issue
+//     the tile loads.
+// Per tile t, phase A: the DMA waves issue tile t+2 into the stage of tile t-2;
+// the score waves run the scores and softmax of tile t (at raised priority while
+// their MFMAs issue), the PV waves the PV of tile t-1, so the score waves'
+// softmax overlaps the PV MFMAs on every SIMD.  [barrier]  Phase B: the score
+// waves publish P(t), its scales and the rows' rescale factors.  [barrier, tile
+// t+1 landed]  Two tiles stay in flight.  A row whose max outgrows its reference
 // by more than kTau moves the reference (one pass, no recomputation): the score
 // wave scales its row sums by 2^(old - new) and publishes that factor, the PV
 // waves scale the row's output accumulators by it before adding the tile.
 // ---------------------------------------------------------------------------
 constexpr int kThreadsR = 768;
+// Sequences of at most this many keys take the second P term.  The E4M3 rounding of P moves a
+// row's output by up to ~2^-4 of the weight its few largest keys carry; over many keys the
+// weights spread and the per-key errors average out (on the ragged speculative-decoding
+// workload the single-term error falls from 5e-2 at 1-2K keys to 2e-2 above 8K).
+constexpr int kLoKeys = 8192;
 constexpr int kRDummy = kStages * kStageBytes;  // 1 KiB: destination of dummy-tile loads
 constexpr int kRP = kRDummy + 1024;              // P codes: [row block 4][half 2][lane 64][16 bytes]
 constexpr int kRScale = kRP + 8192;              // E8M0 scale codes: [row block 4][lane 64] int32
@@ -1566,6 +1573,7 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
   const int n_gmax = min(max(L - qlen_b + gF + p.F, 0), L);
   const int window = WIN ? p.window : 0;
   const int kbase = seq_key0<TILE>(L, qlen_b, window);
+  const bool lo_seg = L <= kLoKeys;
   const int k0 = kbase + sg.u0 * TILE;
   const int k1 = min(kbase + sg.u1 * TILE, n_gmax);
 
@@ -1627,10 +1635,13 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
     int d_key0 = k0, d_pidx0 = 0;
     int d_pg0 = 0, d_pg1 = 0, d_pg2 = 0, d_pg3 = 0;
     int pf0 = 0, pf1 = 0, pf2 = 0, pf3 = 0;
+    // every wave takes part in the block-table refills (workgroup barriers); only the DMA waves
+    // look up pages and set up loads
     auto prefetch_pages = [&](int tt) {
       const int pidx0 = (k0 + tt * TILE) >> p.page_shift;
       constexpr int kFillTiles = FAST ? kBtEntries : (kBtEntries - 3) / 4;
       if (tt > 0 && tt % kFillTiles == 0) bt_fill(pidx0);
+      if (!dma_wave) return;
       pf0 = page_raw(pidx0);
       if constexpr (!FAST) {
         pf1 = page_raw(pidx0 + 1);
@@ -1638,21 +1649,22 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
         pf3 = page_raw(pidx0 + 3);
       }
     };
-    // every wave sets up (the block-table refill inside is a workgroup barrier); the DMA waves issue
     auto dma_setup = [&](int tt) {
       if (tt < ntiles) {
-        const int key0 = k0 + tt * TILE;
-        d_m0 = smem_base + (uint32_t)((tt % kStages) * kStageBytes);
-        d_step = 1024;
-        d_key0 = key0;
-        d_pidx0 = key0 >> p.page_shift;
-        if constexpr (FAST) {
-          d_base = p.kv + ((size_t)clamp_page(pf0) * p.page_size + (key0 & pmask)) * RB;
-        } else {
-          d_pg0 = clamp_page(pf0);
-          d_pg1 = clamp_page(pf1);
-          d_pg2 = clamp_page(pf2);
-          d_pg3 = clamp_page(pf3);
+        if (dma_wave) {
+          const int key0 = k0 + tt * TILE;
+          d_m0 = smem_base + (uint32_t)((tt % kStages) * kStageBytes);
+          d_step = 1024;
+          d_key0 = key0;
+          d_pidx0 = key0 >> p.page_shift;
+          if constexpr (FAST) {
+            d_base = p.kv + ((size_t)clamp_page(pf0) * p.page_size + (key0 & pmask)) * RB;
+          } else {
+            d_pg0 = clamp_page(pf0);
+            d_pg1 = clamp_page(pf1);
+            d_pg2 = clamp_page(pf2);
+            d_pg3 = clamp_page(pf3);
+          }
         }
         if (tt + 1 < ntiles) prefetch_pages(tt + 1);
       } else {
@@ -1686,11 +1698,15 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
         for (int kk = 0; kk < kDmaPerWave; ++kk) dma_issue(kk);
       }
     };
-    // the DMA waves wait for their loads of the next tile (the two younger tiles stay in
-    // flight), every wave for its LDS writes; then the barrier
+    // Phase A is split at the end of the score MFMAs: the PV waves read their V operands, then
+    // wait here, so that their MFMAs run beside the softmax instead of stretching the score
+    // chain (the MFMA pipe is shared, and an issued MFMA is not preempted).  No wait on memory.
+    auto mid_barrier = [&]() { __builtin_amdgcn_s_barrier(); };
+    // the DMA waves wait for their loads of the next tile (the younger tile stays in flight),
+    // every wave for its LDS writes; then the barrier
     auto wait_next = [&]() {
       if (dma_wave) {
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * kDmaPerWave) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kDmaPerWave) : "memory");
       } else {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
@@ -1769,10 +1785,22 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
             if ((uint32_t)(kb + 32 + 8 * (r >> 2) + (r & 3)) >= vis_m) s1[r] = -INFINITY;
           }
         }
-        float mx = -INFINITY;
+        // row max over the lane's 32 scores: a three-input max tree (fmaxf would first quiet every
+        // score, the MFMA results being opaque to the compiler)
+        auto max3 = [](float a, float b, float c) -> float {
+          float r;
+          asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+          return r;
+        };
+        float m9[11];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-        const float rm = xor32_max(mx * p.s_scale_log2);  // row max of the tile, log2 units
+        for (int i = 0; i < 5; ++i) m9[i] = max3(s0[3 * i], s0[3 * i + 1], s0[3 * i + 2]);
+#pragma unroll
+        for (int i = 0; i < 5; ++i) m9[5 + i] = max3(s1[3 * i], s1[3 * i + 1], s1[3 * i + 2]);
+        m9[10] = max3(s0[15], s1[15], m9[9]);
+        const float mx = max3(max3(m9[0], m9[1], m9[2]), max3(m9[3], m9[4], m9[5]), max3(m9[6], m9[7], m9[8]));
+        const float mxx = max3(mx, m9[10], m9[10]);
+        const float rm = xor32_max(mxx * p.s_scale_log2);  // row max of the tile, log2 units
         // The reference is fixed at the row's first visible tile and moves only when a tile's
         // max outgrows it by more than kTau: then everything accumulated so far is scaled by
         // 2^(old - new) (the row sums here, the output accumulators by the PV waves).
@@ -1795,7 +1823,7 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
         // residual is at most 8 (half an E4M3 step in [128, 256]) and half of it fits E2M1's range;
         // with the second term each p is off by at most 2^-7 of its own binade.  O is normalised by
         // the exact sum: the two terms differ from it by less than that.
-        auto four = [&](const v16f& sv, int w2, int& lo) -> int {
+        auto four = [&](const v16f& sv, int w2, int& lo, auto with_lo) -> int {
           const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * w2 + 0], p.s_scale_log2, -off));
           const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * w2 + 1], p.s_scale_log2, -off));
           const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[4 * w2 + 2], p.s_scale_log2, -off));
@@ -1803,6 +1831,7 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
           int wv = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
           wv = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, wv, true);
           lsum += (e0 + e1) + (e2 + e3);
+          if constexpr (!decltype(with_lo)::value) return wv;
           const v2f r0 = __builtin_amdgcn_cvt_pk_f32_fp8(wv, false);
           const v2f r1 = __builtin_amdgcn_cvt_pk_f32_fp8(wv, true);
           // (the conversion divides by its scale: codes of d / 2)
@@ -1818,13 +1847,21 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
           return wv;
         };
         la[0] = la[1] = lb[0] = lb[1] = 0;
+        if (lo_seg) {
 #pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          pa[w2] = four(s0, w2, la[w2 >> 1]);
-          pb[w2] = four(s1, w2, lb[w2 >> 1]);
+          for (int w2 = 0; w2 < 4; ++w2) {
+            pa[w2] = four(s0, w2, la[w2 >> 1], std::true_type{});
+            pb[w2] = four(s1, w2, lb[w2 >> 1], std::true_type{});
+          }
+        } else {
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2) {
+            pa[w2] = four(s0, w2, la[w2 >> 1], std::false_type{});
+            pb[w2] = four(s1, w2, lb[w2 >> 1], std::false_type{});
+          }
         }
         l_acc += __builtin_ldexpf(lsum, -e);
-        sc_code = 127 - e;
+        sc_code = (127 - e) | (lo_seg ? 0x100 : 0);  // bit 8: the PV waves add the second term
       };
       // The second term of P(t) goes into the rope columns of tile t's own stage (bytes 512..575 of
       // its 64 rows): the score waves are done with them once the barrier after the scores has
@@ -1843,6 +1880,7 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
         __builtin_amdgcn_s_setprio(2);  // the score chain is the tile's critical path
         qk(stage(t));
         __builtin_amdgcn_s_setprio(0);
+        mid_barrier();
         softmax(key0, tile_needs_mask(key0));
       };
 
@@ -1854,7 +1892,10 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
         const int s8 = (2 * (rr >> 2) + hs) & 3;
         vaddr0 = kbr * RB + ((dsub ^ s8) * 16) + 8 * c8;  // chunk pair partner: ^ 32
       }
-      auto pv_tile = [&](int t) {
+      // with_dma: the DMA waves issue the loads set up last (dma_setup) between the row blocks,
+      // three, two, two and two, so that they share the SIMD with the MFMAs instead of queueing
+      // ahead of them
+      auto pv_tile = [&](int t, bool with_dma) {
         const lds_t* st = stage(t);
         int va = vaddr0 + 64 * pw;
         asm volatile("" : "+v"(va));
@@ -1875,6 +1916,7 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
           }
         }
         const v8i v0 = vread(va), v1 = vread(va ^ 32);
+        mid_barrier();
         // The four row blocks' P stream past the two V operands, one at a time: each read's
         // address is made opaque where it is used, so that the reads are neither merged nor
         // hoisted together (32 more live registers than the budget allows).
@@ -1884,23 +1926,40 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
           asm volatile("" : "+v"(pa_));
           const v4i x = *(const lds_v4i*)(smem + kRP + 2048 * rb + pa_);
           const v4i y = *(const lds_v4i*)(smem + kRP + 2048 * rb + 1024 + pa_);
-          const int scb = *(const lds_i32*)(smem + kRScale + 256 * rb + (pa_ >> 2));
-          // The E2M1 operand of a column: lane half h takes bytes 8h..8h+7 of the entries of lanes
-          // n and n + 32 (its K-slots are those of E4M3 bytes 16h..16h+15 of both lane halves).
-          const int hb = 8 * (lane >> 5), ln = lane & 31;
-          const v2i l0 = *(const lds_v2i*)(lo_entry(st, 64 * rb + ln) + hb);
-          const v2i l1 = *(const lds_v2i*)(lo_entry(st, 64 * rb + 32 + ln) + hb);
+          const int scw = *(const lds_i32*)(smem + kRScale + 256 * rb + (pa_ >> 2));
+          const int scb = scw & 0xff;
           const v8i pr = v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-          const v8i pl = v8i{l0[0], l0[1], l1[0], l1[1], 0, 0, 0, 0};
           o[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v0, pr, o[rb], 0, 0, 0, 127, 0, scb);
           o[4 + rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v1, pr, o[4 + rb], 0, 0, 0, 127, 0, scb);
-          // the residual term: B in E2M1 (blgp 4), twice the E4M3 term's scale
-          o[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v0, pl, o[rb], 0, 4, 0, 127, 0, scb + 1);
-          o[4 + rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v1, pl, o[4 + rb], 0, 4, 0, 127, 0, scb + 1);
-          // the MFMAs stay here (left alone, the compiler sinks them past the barrier that
-          // follows, keeping every P operand live across it)
-          asm volatile("" : "+v"(o[rb]), "+v"(o[4 + rb]));
+          if (__builtin_amdgcn_readfirstlane(scw) & 0x100) {
+            // The residual term: B in E2M1 (blgp 4), twice the E4M3 term's scale.  The E2M1 operand
+            // of a column: lane half h takes bytes 8h..8h+7 of the entries of lanes n and n + 32
+            // (its K-slots are those of E4M3 bytes 16h..16h+15 of both lane halves).
+            const int hb = 8 * (lane >> 5), ln = lane & 31;
+            const v2i l0 = *(const lds_v2i*)(lo_entry(st, 64 * rb + ln) + hb);
+            const v2i l1 = *(const lds_v2i*)(lo_entry(st, 64 * rb + 32 + ln) + hb);
+            const v8i pl = v8i{l0[0], l0[1], l1[0], l1[1], 0, 0, 0, 0};
+            o[rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v0, pl, o[rb], 0, 4, 0, 127, 0, scb + 1);
+            o[4 + rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v1, pl, o[4 + rb], 0, 4, 0, 127, 0, scb + 1);
+          }
+          // The MFMAs stay in the tile (left alone, the compiler sinks them past the barrier that
+          // follows, keeping every P operand live across it): the previous row block's results
+          // are pinned here, one block late, so the pin finds them complete instead of waiting
+          // for the MFMAs just issued.
+          if (rb > 0) asm volatile("" : "+v"(o[rb - 1]), "+v"(o[3 + rb]));
+          if (with_dma && dma_wave) {
+            static_assert(kDmaPerWave == 9, "loads per row block below");
+            if (rb == 0) {
+              dma_issue(0);
+              dma_issue(1);
+              dma_issue(2);
+            } else {
+              dma_issue(2 * rb + 1);
+              dma_issue(2 * rb + 2);
+            }
+          }
         }
+        asm volatile("" : "+v"(o[3]), "+v"(o[7]));
       };
 
       // ---- prologue: Q through ring stages 2-3, tiles 0 and 1 ----
@@ -1942,25 +2001,39 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
       }
       if (ntiles == 1) zero_tail(0);
       issue_tile(2);
-      issue_tile(3);
-      if constexpr (SCORE) score_tile(0);
+      if constexpr (SCORE) {
+        score_tile(0);
+      } else {
+        mid_barrier();
+      }
       lds_barrier();
       if constexpr (SCORE) publish(0);
       wait_next();  // P(0) visible, tile 1 landed
 
       for (int t = 1; t < ntiles; ++t) {
         if (t == ntiles - 1) zero_tail(t);
+        // Tile t+2 goes into the stage of tile t-2, free since the PV of t-2 (the last iteration):
+        // the DMA waves issue it during their PV work, off the score waves' path.
+        // (pages shorter than a tile take four page registers: their loads go out at once, here)
+        if constexpr (FAST) {
+          dma_setup(t + 2);
+        } else {
+          issue_tile(t + 2);
+        }
         if constexpr (SCORE) {
           score_tile(t);
         } else {
-          pv_tile(t - 1);
+          pv_tile(t - 1, FAST);
         }
-        lds_barrier();  // PV of tile t-1 is done: the P buffer and the stage of tile t-1 are free
+        lds_barrier();  // PV of tile t-1 is done: the P buffer is free
         if constexpr (SCORE) publish(t);
-        issue_tile(t + 3);
         wait_next();  // P(t) visible, tile t+1 landed
       }
-      if constexpr (!SCORE) pv_tile(ntiles - 1);
+      if constexpr (SCORE) {
+        mid_barrier();
+      } else {
+        pv_tile(ntiles - 1, false);
+      }
       // the dummy loads must land before LDS is reused
       if (dma_wave) {
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
