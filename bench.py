@@ -153,6 +153,64 @@ def _counter_avg(path, counter, name_part):
     return sum(vals) / len(vals), len(vals)
 
 
+COUNTER_PASSES = {
+    "cnt_a": ["GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F8",
+              "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS",
+              "SQ_WAVE_CYCLES"],
+    "cnt_b": ["SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_INSTS_SALU",
+              "SQ_INSTS_MFMA", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F16"],
+}
+N_XCD, N_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def _counters(path, name_part):
+    """Per-dispatch means of every counter in a rocprofv3 --pmc run for kernels matching name_part, with the
+    dispatch's own duration (ns) from the same run."""
+    per = {}
+    dur = {}
+    for r in _csv_rows(path):
+        if name_part not in r["Kernel_Name"]:
+            continue
+        per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    out = {k: sum(v) / len(v) for k, v in per.items()}
+    out["_duration_ns"] = sum(dur.values()) / len(dur) if dur else None
+    out["_dispatches"] = len(dur)
+    return out
+
+
+def derived_counters(c: dict) -> dict:
+    """Clock, MFMA busy fraction, achieved MFMA rate and LDS figures from one dispatch's counters.
+    GRBM_GUI_ACTIVE counts GPU-busy cycles on each XCD (summed over the 8); SQ_VALU_MFMA_BUSY_CYCLES sums
+    matrix-core busy cycles over all 1024 SIMDs; one MOPS unit is 512 flops."""
+    d = {}
+    ns = c.get("_duration_ns")
+    gui = c.get("GRBM_GUI_ACTIVE")
+    if gui and ns:
+        cyc = gui / N_XCD
+        d["cycles_per_xcd"] = round(cyc)
+        d["clock_ghz"] = round(cyc / ns, 3)
+        if c.get("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+            d["mfma_busy_frac"] = round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_SIMD), 4)
+    mops = sum(c.get(k, 0.0) for k in ("SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                                       "SQ_INSTS_VALU_MFMA_MOPS_F16"))
+    if mops and ns:
+        d["mfma_tflops"] = round(mops * 512 / (ns * 1e-9) / 1e12, 1)
+    for k in ("SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+              "SQ_INSTS_SALU", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_BUSY_CYCLES",
+              "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_ACTIVE_INST_VALU"):
+        if k in c:
+            d[k] = c[k]
+    if c.get("SQ_ACTIVE_INST_LDS"):
+        d["lds_bank_conflict_share"] = round(c.get("SQ_LDS_BANK_CONFLICT", 0.0) / c["SQ_ACTIVE_INST_LDS"], 4)
+    if c.get("SQ_WAVE_CYCLES"):
+        if "SQ_WAIT_ANY" in c:
+            d["wait_any_share"] = round(c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"], 4)
+        if "SQ_WAIT_INST_ANY" in c:
+            d["wait_inst_share"] = round(c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"], 4)
+    return d
+
+
 def _trace_regions(path, steps=50):
     """Per-region kernel timings from the dispatch trace of one bench.py run, in the order bench.py runs
     them: steps (split-KV then merge), split-KV alone back to back, merge alone back to back.  Each
@@ -216,6 +274,21 @@ def summarize_profile(d: str, workload: str):
                                  "calls": int(st[0]["Calls"]) if st else None}
     kp = out["kernels"]["mla_split_kv_partial"]
     out["hbm_bytes_per_launch"] = kp["fetch_bytes"] + kp["write_bytes"]
+    cnt = {}
+    for short, part in (("mla_split_kv_partial", "mla_split_kv"), ("mla_combine", "mla_combine")):
+        raw = {}
+        for pas in COUNTER_PASSES:
+            if os.path.isdir(os.path.join(d, pas)):
+                c = _counters(os.path.join(d, pas), part)
+                dur = c.pop("_duration_ns")
+                c.pop("_dispatches")
+                raw.update(c)
+                raw.setdefault("_duration_ns", dur)
+        if raw:
+            cnt[short] = {"raw": {k: v for k, v in raw.items() if not k.startswith("_")},
+                          "duration_ns_under_counters": raw.get("_duration_ns"), "derived": derived_counters(raw)}
+    if cnt:
+        out["counters"] = cnt
     out["regions"] = _trace_regions(os.path.join(d, "trace"))
     base = os.path.join(ROOT, "profiles")
     with open(os.path.join(base, f"mla_split_kv_partial_{workload}_traffic.json"), "w") as f:
@@ -249,16 +322,36 @@ def summarize_profile(d: str, workload: str):
               "| kernel | read MB | written MB |", "|---|---|---|"]
     for k, v in out["kernels"].items():
         lines.append(f"| {k} | {v['fetch_bytes'] / 1e6:.2f} | {v['write_bytes'] / 1e6:.2f} |")
+    if cnt:
+        lines += ["", "Counters (`--pmc`, two passes of one `bench.py --steps 5 --warmup 2` run each), per dispatch, "
+                  "with the dispatch's own duration in the same run:", "",
+                  "- clock = GRBM_GUI_ACTIVE / 8 XCDs / duration",
+                  "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs)",
+                  "- MFMA rate = SQ_INSTS_VALU_MFMA_MOPS_{F8,BF16,F16} x 512 flops / duration",
+                  "- LDS bank-conflict share = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS (cycles)",
+                  "- wait shares = SQ_WAIT_ANY, SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES", "",
+                  "| kernel | us | clock GHz | MFMA busy | MFMA TFLOP/s | LDS insts | LDS conflict share | "
+                  "VALU insts | wait share |", "|---|---|---|---|---|---|---|---|---|"]
+        for k, v in cnt.items():
+            dv = v["derived"]
+            us = (v["duration_ns_under_counters"] or 0) / 1e3
+            lines.append(f"| {k} | {us:.1f} | {dv.get('clock_ghz', '')} | {dv.get('mfma_busy_frac', '')} | "
+                         f"{dv.get('mfma_tflops', '')} | {dv.get('SQ_INSTS_LDS', 0):.4g} | "
+                         f"{dv.get('lds_bank_conflict_share', '')} | {dv.get('SQ_INSTS_VALU', 0):.4g} | "
+                         f"{dv.get('wait_any_share', '')} |")
     lines += ["", f"Kernel code sha256/16 (comments and whitespace removed): `{out['kernel_code_sha256_16']}`", "", "Commands (repository root):", "",
               "```",
               f"rocprofv3 --kernel-trace --stats -d {d}/trace -o run --output-format csv -- "
-              f"python3 bench.py --workload {workload} --steps 50 --warmup 50 --no-cpu-baseline",
+              f"python3 bench.py --workload {workload} --steps 50 --warmup 50 --no-cpu-baseline --no-configs --no-achievable",
               f"rocprofv3 --pmc FETCH_SIZE -d {d}/fetch -o run --output-format csv -- "
-              f"python3 bench.py --workload {workload} --steps 5 --warmup 2 --no-cpu-baseline",
+              f"python3 bench.py --workload {workload} --steps 5 --warmup 2 --warmup-ms 0 --no-cpu-baseline --no-configs --no-achievable",
               f"rocprofv3 --pmc WRITE_SIZE -d {d}/write -o run --output-format csv -- "
-              f"python3 bench.py --workload {workload} --steps 5 --warmup 2 --no-cpu-baseline",
+              f"python3 bench.py --workload {workload} --steps 5 --warmup 2 --warmup-ms 0 --no-cpu-baseline --no-configs --no-achievable",
               f"rocprofv3 --pmc FETCH_SIZE -d {d}/cal_fetch -o run --output-format csv -- python3 bench.py --copy-calibration",
               f"rocprofv3 --pmc WRITE_SIZE -d {d}/cal_write -o run --output-format csv -- python3 bench.py --copy-calibration",
+              *[f"rocprofv3 --pmc {' '.join(cs)} -d {d}/{pas} -o run --output-format csv -- python3 bench.py "
+                f"--workload {workload} --steps 5 --warmup 2 --warmup-ms 0 --no-cpu-baseline --no-configs --no-achievable"
+                for pas, cs in COUNTER_PASSES.items() if os.path.isdir(os.path.join(d, pas))],
               f"python3 bench.py --summarize-profile {d} --workload {workload}",
               "```", ""]
     with open(os.path.join(base, f"mla_split_kv_partial_{workload}.md"), "w") as f:
@@ -272,20 +365,31 @@ def cpu_baseline(x, max_threads: int):
 
     import oracle
 
-    threads = max(1, min(max_threads, os.cpu_count() or 1, x.B * x.q_len))
+    nproc = os.cpu_count() or 1
+    threads = max(1, min(max_threads, nproc, x.B * x.q_len))
     frac = 1.0 if x.name.startswith("agentic") else 0.05
-    lens = np.maximum(1, (x.seq_lens.astype(np.int64) * frac).astype(np.int64)).astype(np.int32)
-    oracle.mla_decode(x.q[:1, :1, :1], x.kv_cache, x.block_table[:1], np.minimum(lens[:1], 64), dtype=x.dtype,
-                      softmax_scale=x.softmax_scale, q_scale=x.q_scale, kv_scale=x.kv_scale, num_threads=1)
-    t0 = time.perf_counter()
-    oracle.mla_decode(x.q, x.kv_cache, x.block_table, lens, dtype=x.dtype, softmax_scale=x.softmax_scale,
-                      q_scale=x.q_scale, kv_scale=x.kv_scale, num_threads=threads)
-    dt = time.perf_counter() - t0
     e = 1 if x.kv_cache.dtype == np.uint8 else 2
-    kv = float(lens.astype(np.int64).sum()) * 576 * e
-    return {"value": kv / dt / 1e12, "unit": "TB/s", "cores": threads, "kind": "oracle",
-            "sample": f"all {x.B * x.q_len} (sequence, query token) rows of the workload, first {frac:.0%} of each "
-                      f"sequence's keys ({int(lens.sum())} keys), fp64, {dt:.2f} s wall"}
+
+    def timed(f, nthreads):
+        lens = np.maximum(1, (x.seq_lens.astype(np.int64) * f).astype(np.int64)).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.mla_decode(x.q, x.kv_cache, x.block_table, lens, dtype=x.dtype, softmax_scale=x.softmax_scale,
+                          q_scale=x.q_scale, kv_scale=x.kv_scale, num_threads=nthreads)
+        dt = time.perf_counter() - t0
+        return float(lens.astype(np.int64).sum()) * 576 * e / dt / 1e12, int(lens.sum()), dt
+
+    oracle.mla_decode(x.q[:1, :1, :1], x.kv_cache, x.block_table[:1], np.minimum(x.seq_lens[:1], 64), dtype=x.dtype,
+                      softmax_scale=x.softmax_scale, q_scale=x.q_scale, kv_scale=x.kv_scale, num_threads=1)
+    v, keys, dt = timed(frac, threads)
+    # the same rows on one thread, over a quarter of that prefix (the rate is per key)
+    v1, keys1, dt1 = timed(frac / 4, 1)
+    return {"value": v, "unit": "TB/s", "cores": threads, "nproc": nproc, "kind": "oracle",
+            "sample": f"all {x.B * x.q_len} (sequence, query token) rows of the workload, the first {frac:.0%} of "
+                      f"each sequence's keys ({keys} keys; a prefix, so the rate is per KV byte read), fp64, "
+                      f"{dt:.2f} s wall on {threads} threads of the {nproc} the host reports",
+            "value_1core": v1,
+            "sample_1core": f"the same rows over the first {frac / 4:.2%} of each sequence's keys ({keys1} keys), "
+                            f"one thread, {dt1:.2f} s wall"}
 
 
 def bench_pack(args):
@@ -396,53 +500,45 @@ def bench_ragged(args):
                       "kernels_ms": {"split_kv_partial": round(part, 5)}}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--warmup-ms", type=float, default=250.0,
-                    help="keep warming up until this much wall time has passed (the GPU's clocks settle)")
-    ap.add_argument("--workload", default="agentic_b4_q4_h32_fp8_80k")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-threads", type=int, default=16)
-    ap.add_argument("--num-splits", type=int, default=0, help="override the planned KV slice count")
-    ap.add_argument("--partial-fp32", action="store_true", help="keep split partials in fp32 (default bf16)")
-    ap.add_argument("--kernel", type=int, default=0,
-                    help="E4M3 split-KV kernel: 0 default, 1 four-wave, 2 twelve-wave role-specialised")
-    ap.add_argument("--merge", type=int, default=0, help="merge kernel: 0 wide (default), 1 workgroup per row")
-    ap.add_argument("--copy-calibration", action="store_true", help="run the counter-calibration copy and exit")
-    ap.add_argument("--summarize-profile", metavar="DIR", help="summarise rocprofv3 runs under DIR into profiles/")
-    ap.add_argument("--pack-tokens", type=int, default=0,
-                    help="time the fused K/V pack + FP8 quantise kernel on this many tokens instead of the decode")
-    args = ap.parse_args()
-    if args.summarize_profile:
-        summarize_profile(args.summarize_profile, args.workload)
-        return
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.gpus != 1:
-        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
-              "sequences are independent, so the decode would shard by batch, each GPU with its own sequences and cache", file=sys.stderr)
-        sys.exit(2)
-    if args.pack_tokens > 0:
-        bench_pack(args)
-        return
-    if args.workload.startswith("ragged_prefill"):
-        bench_ragged(args)
-        return
+# the five benchmark configurations, in order (the headline is the second: q_len 4, 80K keys, B 4)
+CONFIG_WORKLOADS = ["tiny_b1_h16_bf16", "agentic_b4_q4_h32_fp8_80k", "agentic_b16_q4_h32_fp8_80k",
+                    "dsv3_b64_q1_h128_bf16_ragged", "spec_b128_q4_h64_fp8_ragged"]
+ACHIEVABLE_NOTE = ("read bandwidth a plain streaming kernel reaches on this GPU: torch sum over a 4 GiB "
+                   "buffer, best of 5 (HBM only, no compute)")
 
+
+def achievable_read_gbs() -> float:
+    """Streaming read bandwidth with no compute: a reduction over a buffer far larger than the 256 MB cache."""
+    import torch
+
+    n = (4 << 30) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    best = 0.0
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        x.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, n * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del x
+    torch.cuda.empty_cache()
+    return round(best, 1)
+
+
+def measure_decode(workload: str, args, *, steps: int, warmup: int, warmup_ms: float, with_graph: bool) -> dict:
+    """Time one decode workload: K steps back to back (both kernels), then each kernel alone, and with
+    with_graph the same steps replayed from one captured HIP graph.  Returns the headline line and a
+    compact record for the configs object."""
     import numpy as np
     import torch
 
     import mla_inputs as mi
     import mla_paged_kv_decode_amd as mla
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
-    x = mi.workload_inputs(args.workload)
+    print(f"[bench] generating {workload}", file=sys.stderr, flush=True)
+    x = mi.workload_inputs(workload)
     alg = algorithmic(x)
     tdt_of = {mi.BF16: torch.bfloat16, mi.FP16: torch.float16, mi.FP8_E4M3: torch.float8_e4m3fn}
     tq, tdt = tdt_of[mi.q_format(x.dtype)], tdt_of[mi.kv_format(x.dtype)]
@@ -522,9 +618,9 @@ def main():
         return e0.elapsed_time(e1) / K, time.perf_counter() - t0
 
     prepare(0)
-    n_warm, warm_ms = warm_up(step, args.warmup, args.warmup_ms)
+    n_warm, warm_ms = warm_up(step, warmup, warmup_ms)
 
-    K = args.steps
+    K = steps
     # the step: both kernels, K times back to back (the headline figure)
     t0 = time.perf_counter()
     ms_per_step = timed_eager(0, n_warm)
@@ -533,45 +629,49 @@ def main():
     part_avg = timed_eager(1, n_warm + K)
     merge_avg = timed_eager(2, n_warm + 2 * K) if num_splits > 1 else 0.0
     # the same K steps captured into one HIP graph and replayed (reported beside the headline)
-    graph_ms, _ = timed_graph(0, n_warm)
+    graph_ms = timed_graph(0, n_warm)[0] if with_graph else None
 
     value = alg["kv_bytes"] / (ms_per_step * 1e-3) / 1e12
     # the split-KV kernel against the roofline that binds it: HBM bytes at 8 TB/s or MFMA flops at
-    # the dense peak of its operand type, whichever takes longer
+    # the dense peak of its operand type, whichever takes longer; the same for the whole step
     kern_gbs = alg["bytes"] / (part_avg * 1e-3) / 1e9
     kern_tfs = alg["flops"] / (part_avg * 1e-3) / 1e12
+    step_gbs = alg["bytes"] / (ms_per_step * 1e-3) / 1e9
     mfma_peak = MFMA_PEAK_TFLOPS[x.dtype]
     mfma_bound = alg["flops"] / (mfma_peak * 1e12) > alg["bytes"] / (HBM_PEAK_GBS * 1e9)
-    traffic = load_traffic(args.workload)
+    traffic = load_traffic(workload)
     tflops = alg["flops"] / (ms_per_step * 1e-3) / 1e12
-    pages_us = PAGES_US.get(args.workload)
+    frac_step = tflops / mfma_peak if mfma_bound else step_gbs / HBM_PEAK_GBS
+    pages_us = PAGES_US.get(workload)
     line = {
         "metric": METRIC,
         "value": round(value, 4),
         "unit": "TB/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "warmup_steps_run": n_warm,
         "warmup_ms": round(warm_ms, 1),
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
-        "graph_us_per_step": round(graph_ms * 1e3, 2),
+        "graph_us_per_step": round(graph_ms * 1e3, 2) if graph_ms is not None else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(pages_us / (ms_per_step * 1e3), 4) if pages_us else None,
         "dtype": DTYPE_NAMES[x.dtype],
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": B, "q_len": q_len, "num_heads": H, "d_qk": 576, "d_v": 512,
+        "config": {"workload": workload, "batch": B, "q_len": q_len, "num_heads": H, "d_qk": 576, "d_v": 512,
                    "page_size": x.page_size, "max_seq_len": x.max_seq_len,
                    "total_kv_tokens": int(x.seq_lens.astype(np.int64).sum()), "num_splits": num_splits,
                    "kv_pool_copies": copies, "parallelism": "single GPU"},
+        # frac: the split-KV kernel alone (its own launches back to back); frac_step: the whole step
+        # (both kernels and the gaps between them), the figure the 70 % target is judged on
         "roofline": ({"bound": "mfma", "kernel": "mla_split_kv_partial", "achieved": round(kern_tfs, 1),
                       "peak": mfma_peak, "unit": "TFLOP/s", "frac": round(kern_tfs / mfma_peak, 4)}
                      if mfma_bound else
                      {"bound": "hbm", "kernel": "mla_split_kv_partial", "achieved": round(kern_gbs, 1),
                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4)})
-        | {"traffic": traffic, "algorithmic_bytes_per_launch": alg["bytes"],
+        | {"traffic": traffic, "frac_step": round(frac_step, 4), "algorithmic_bytes_per_launch": alg["bytes"],
            "algorithmic_flops_per_launch": alg["flops"], "avg_launch_ms": round(part_avg, 5),
            "hbm_frac": round(kern_gbs / HBM_PEAK_GBS, 4), "mfma_frac": round(kern_tfs / mfma_peak, 4)},
         "kernels_ms": {"split_kv_partial": round(part_avg, 5), "merge": round(merge_avg, 5)},
@@ -579,7 +679,80 @@ def main():
         "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS[x.dtype], 4),
         "wall_s_timed": round(wall, 4),
     }
+    compact = {"us_per_step": round(ms_per_step * 1e3, 2), "kv_tb_s": round(value, 4),
+               "bytes_tb_s": round(step_gbs / 1e3, 4), "tflop_s": round(tflops, 1), "dtype": DTYPE_NAMES[x.dtype],
+               "bound": "mfma" if mfma_bound else "hbm", "frac_step": round(frac_step, 4),
+               "frac_split_kv": line["roofline"]["frac"],
+               "kernels_us": {"split_kv": round(part_avg * 1e3, 2), "merge": round(merge_avg * 1e3, 2)},
+               "num_splits": num_splits, "steps": K,
+               "shape": {"batch": B, "q_len": q_len, "num_heads": H,
+                         "total_kv_tokens": int(x.seq_lens.astype(np.int64).sum())}}
+    del kvs, kv0, q, bt, sl, out, lse, ws, calls
+    return {"line": line, "compact": compact}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup-ms", type=float, default=250.0,
+                    help="keep warming up until this much wall time has passed (the GPU's clocks settle)")
+    ap.add_argument("--workload", default="agentic_b4_q4_h32_fp8_80k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="time only --workload, not every configuration")
+    ap.add_argument("--no-achievable", action="store_true", help="skip the streaming-read reference figure")
+    ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--num-splits", type=int, default=0, help="override the planned KV slice count")
+    ap.add_argument("--partial-fp32", action="store_true", help="keep split partials in fp32 (default bf16)")
+    ap.add_argument("--kernel", type=int, default=0,
+                    help="E4M3 split-KV kernel: 0 default, 1 four-wave, 2 twelve-wave role-specialised")
+    ap.add_argument("--merge", type=int, default=0, help="merge kernel: 0 wide (default), 1 workgroup per row")
+    ap.add_argument("--copy-calibration", action="store_true", help="run the counter-calibration copy and exit")
+    ap.add_argument("--summarize-profile", metavar="DIR", help="summarise rocprofv3 runs under DIR into profiles/")
+    ap.add_argument("--pack-tokens", type=int, default=0,
+                    help="time the fused K/V pack + FP8 quantise kernel on this many tokens instead of the decode")
+    args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.workload)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1:
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
+              "sequences are independent, so the decode would shard by batch, each GPU with its own sequences and cache", file=sys.stderr)
+        sys.exit(2)
+    if args.pack_tokens > 0:
+        bench_pack(args)
+        return
+    if args.workload.startswith("ragged_prefill"):
+        bench_ragged(args)
+        return
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    head = measure_decode(args.workload, args, steps=args.steps, warmup=args.warmup, warmup_ms=args.warmup_ms,
+                          with_graph=True)
+    line = head["line"]
+    if not args.no_configs:
+        # every benchmark configuration, timed the same way (fewer steps; no graph replay)
+        line["configs"] = {}
+        for name in CONFIG_WORKLOADS:
+            if name == args.workload:
+                line["configs"][name] = head["compact"]
+                continue
+            r = measure_decode(name, args, steps=min(args.steps, 20), warmup=min(args.warmup, 10),
+                               warmup_ms=min(args.warmup_ms, 100.0), with_graph=False)
+            line["configs"][name] = r["compact"]
+            torch.cuda.empty_cache()
+    if not args.no_achievable:
+        line["roofline"]["achievable_gbs"] = achievable_read_gbs()
+        line["roofline"]["achievable_note"] = ACHIEVABLE_NOTE
     if not args.no_cpu_baseline:
+        import mla_inputs as mi
+
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         xb = mi.workload_inputs(args.workload)
         line["cpu_baseline"] = cpu_baseline(xb, args.cpu_threads)

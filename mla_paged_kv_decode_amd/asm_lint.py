@@ -11,9 +11,10 @@ instantiation and reports:
     the register allocator inserted);
   * an MFMA that reads a VGPR written by a VALU instruction fewer than
     VALU_TO_MFMA_WAITS wait states earlier;
-  * a scratch (spill) access inside the function's innermost loop: a spill
-    reload there is a vector-memory load, and waiting for it waits for every
-    KV tile load in flight, once per tile.
+  * a scratch (spill) access inside the hot loop (the deepest loop level that
+    holds MFMAs, and loops nested in it): a spill reload there is a vector-memory
+    load, and waiting for it waits for every KV tile load in flight, once per
+    tile.
 
 Wait states are counted conservatively: one per instruction, N+1 per `s_nop N`;
 stalls are not credited.  A label resets the tracking (control flow merges).
@@ -86,20 +87,39 @@ def lint_function(lines: list[str]) -> list[str]:
     return problems
 
 
-def loop_spills(lines: list[str]) -> list[str]:
-    """Scratch accesses in blocks at the deepest loop level the compiler annotated."""
-    depth, deepest, found = 0, 0, []
-    for i, ln in enumerate(lines):
+def block_depths(lines: list[str]) -> list[int]:
+    """Loop depth of every line, from the compiler's block annotations: a label line (`.LBBx_y:` or
+    `; %bb.N:`) starts a block, `Depth=N` on it or on the comment lines right after it (a loop
+    header's own `=> This Loop Header: Depth=N`) gives the block's depth, no annotation means 0."""
+    depth, out, in_header = 0, [], False
+    for ln in lines:
         s = ln.strip()
-        m = re.match(r"^\.LBB\d+_\d+:.*Depth=(\d+)", s)
-        if m:
-            depth = int(m.group(1))
-            deepest = max(deepest, depth)
-        elif re.match(r"^\.LBB\d+_\d+:", s):
-            depth = 0
-        elif s.startswith("scratch_"):
-            found.append((depth, i, s))
-    return [f"line {i}: '{s[:60]}' inside the innermost loop" for d, i, s in found if deepest and d == deepest]
+        if re.match(r"^(\.LBB\d+_\d+:|; %bb\.\d+:)", s):
+            m = re.search(r"Depth=(\d+)", s)
+            depth = int(m.group(1)) if m else 0
+            in_header = True
+        elif in_header and s.startswith(";"):
+            m = re.search(r"Loop Header: Depth=(\d+)", s)
+            if m:
+                depth = int(m.group(1))
+        else:
+            in_header = False
+        out.append(depth)
+    return out
+
+
+def loop_spills(lines: list[str]) -> list[str]:
+    """Scratch accesses inside the hot loop: the loop blocks at the deepest level that holds MFMAs (the
+    tile loop), and any loop nested in them.  Spills before or after that loop cost once per segment."""
+    depths = block_depths(lines)
+    hot = 0
+    for ln, d in zip(lines, depths):
+        if d and ln.strip().startswith("v_mfma"):
+            hot = max(hot, d)
+    if not hot:
+        return []
+    return [f"line {i}: '{ln.strip()[:60]}' inside the innermost loop"
+            for i, (ln, d) in enumerate(zip(lines, depths)) if d >= hot and ln.strip().startswith("scratch_")]
 
 
 def lint(asm_text: str, name_part: str = "mla_split_kv") -> dict:

@@ -35,15 +35,33 @@ def test_mfma_accumulator_chain_is_not_a_hazard():
     assert _lint(chain) == []
 
 
-def test_spill_in_innermost_loop_is_flagged():
+def test_spill_in_the_mfma_loop_is_flagged():
+    # the tile loop (depth 2, holds the MFMAs) with a zeroing loop nested in it (depth 3) inside the
+    # segment loop (depth 1): spills in the tile loop or the loop nested in it are flagged, spills in
+    # the segment loop or outside every loop are not
     body = (".LBB2_1:  ; =>This Loop Header: Depth=1\n"
             "\tscratch_load_dword v3, off, off offset:4\n"
-            ".LBB2_2:  ;   Parent Loop BB2_1 Depth=2\n"
+            ".LBB2_2:  ;   Parent Loop BB2_1 Depth=1\n"
+            "           ; =>  This Loop Header: Depth=2\n"
+            "\tv_mfma_f32_32x32x16_bf16 a[0:15], v[0:3], v[4:7], a[0:15]\n"
             "\tscratch_load_dwordx4 v[18:21], off, off\n"
-            ".LBB2_3:\n"
+            ".LBB2_3:  ;   Parent Loop BB2_2 Depth=2\n"
+            "           ; =>    This Inner Loop Header: Depth=3\n"
+            "\tscratch_load_dword v9, off, off offset:8\n"
+            "; %bb.4:  ;   in Loop: Header=BB2_2 Depth=2\n"
+            "\tscratch_load_dword v10, off, off offset:12\n"
+            ".LBB2_5:\n"
             "\tscratch_store_dword off, v3, off\n")
     problems = _lint(body)
-    assert len(problems) == 1 and "scratch_load_dwordx4" in problems[0]
+    assert len(problems) == 3
+    assert "scratch_load_dwordx4" in problems[0] and "v9" in problems[1] and "v10" in problems[2]
+
+
+def test_spill_in_a_loop_without_mfmas_is_allowed():
+    body = (".LBB2_1:  ; =>This Loop Header: Depth=1\n"
+            "\tscratch_load_dword v3, off, off offset:4\n"
+            "\tv_add_u32_e32 v1, v2, v3\n")
+    assert _lint(body) == []
 
 
 def test_spill_outside_loops_is_allowed():
