@@ -33,7 +33,7 @@ struct PartialParams {
   float* lse;                // [B, q_len, H] or nullptr
   void* part_o;              // [G + B][q_len * H][512] fp32 or bf16
   float* part_lse;           // [G + B][q_len * H]
-  int32_t* meta;             // [U][B][2]: first and last KV slice of workgroup row u touching sequence b; then int64 T[U]
+  int32_t* meta;             // [U][B][2]: first and last KV slice of workgroup row u touching sequence b; then int64 C[U]
   int32_t B, q_len, H, F, H_eff, q_len_eff, m_tiles, U, G;
   int32_t xcd_map;           // 1: slices are dealt to the XCDs in turn, each slice's workgroups on one XCD
   int32_t u_major;           // 1: workgroup ids run over the slices of one query group first (many groups)
@@ -45,6 +45,10 @@ struct PartialParams {
   const int32_t* cu_q;       // ragged batch: [B+1] cumulative new-token counts (device), or nullptr
   int32_t total_q;           // ragged batch: token rows of q / out
   int32_t kernel;            // E4M3: 1 the four-wave kernel, 2 the role-specialised kernel, 0 the default
+  // Work partition in cost units of a quarter tile: a (sequence, query group) pair costs seg_cost
+  // (the fixed work of a segment) plus 4 per tile, or lo_cost per tile for E4M3 sequences that take
+  // the second P term (set per kernel at launch)
+  int32_t seg_cost, lo_cost;
 };
 constexpr int kDefaultFp8Kernel = 2;
 

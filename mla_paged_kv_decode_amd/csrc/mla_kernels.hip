@@ -355,6 +355,8 @@ __device__ __forceinline__ void store_out(const v4i& v, v4i* dst, bool final_out
 // Every (slice, sequence) intersection is one segment; its partial lives in
 // workspace slot w + b (unique along the monotone staircase of segments).
 // ---------------------------------------------------------------------------
+// Slice w of a row whose work costs C starts at position w C / G; position x lies in slice
+// slice_of_unit(x, C, G).
 __device__ __forceinline__ long long slice_start(long long w, long long T, int G) { return (w * T) / G; }
 __device__ __forceinline__ int slice_of_unit(long long u, long long T, int G) {
   return (int)(((u + 1) * (long long)G - 1) / T);
@@ -2173,54 +2175,69 @@ __device__ __forceinline__ void for_each_segment(const PartialParams& p, int tid
   const int g = u % p.q_len_eff;
   const int mt = u / p.q_len_eff;
 
-  // ---- total work T (units) of this row and the slice's first sequence ----
-  // Every wave computes the same answer on its own (no LDS, no barrier): lane
-  // i sums the units of sequences [i*kper, (i+1)*kper), one wave-wide prefix
-  // sum gives T and each lane's first unit, and the lane whose range holds the
-  // slice's first unit is found by ballot.
+  // ---- the row's work in cost units, and the slice's first sequence ----
+  // Sequence b of this row holds n_b units (tiles).  It costs c_b per unit: 4, or p.lo_cost for
+  // an E4M3 sequence that takes the second P term; every sequence but the first also costs
+  // p.seg_cost, the fixed work (Q load, pipeline fill, epilogue) of the extra segment its start
+  // adds to the slice it starts in.  The slices cut the row's total cost C evenly, and unit i of b
+  // belongs to the slice holding its position S_b + z_b + c_b i (S_b: the cost of the sequences
+  // before b, z_b its fixed cost), so slices full of costlier units or of short sequences get fewer.
+  // Every wave computes the same answer on its own (no LDS, no barrier): lane i sums the costs of
+  // sequences [i*kper, (i+1)*kper), one wave-wide prefix sum gives C and each lane's first
+  // position, and the lane whose range holds the slice's start is found by ballot.
   const int kper = (p.B + 63) >> 6;
   const int bl0 = min(lane * kper, p.B), bl1 = min(bl0 + kper, p.B);
-  long long own = 0;
   const int window = WIN ? p.window : 0;
-  for (int bb = bl0; bb < bl1; ++bb) own += group_units<UK>(p, bb, g, window);
+  auto unit_cost = [&](int bb) -> int {
+    return p.lo_cost != 4 && ((cint_t*)p.seq_lens)[bb] <= kLoKeys ? p.lo_cost : 4;
+  };
+  long long own = 0;
+  auto fixed_cost = [&](int bb) -> int { return bb > 0 ? p.seg_cost : 0; };
+  for (int bb = bl0; bb < bl1; ++bb) own += fixed_cost(bb) + (long long)unit_cost(bb) * group_units<UK>(p, bb, g, window);
   const long long incl = wave_incl_scan_ll(own);
-  const long long T = readlane_ll(incl, 63);
-  // the merge needs T to recognise empty slices (they write no partials)
+  const long long C = readlane_ll(incl, 63);
   int32_t* meta_u = p.meta != nullptr ? p.meta + 2 * (size_t)u * p.B : nullptr;
-  if (w == 0 && tid == 0 && meta_u != nullptr) ((long long*)(p.meta + 2 * (size_t)p.U * p.B))[u] = T;
-  const long long t0 = slice_start(w, T, p.G), t1 = slice_start(w + 1, T, p.G);
-  if (t0 >= t1) return;
+  if (w == 0 && tid == 0 && meta_u != nullptr) ((long long*)(p.meta + 2 * (size_t)p.U * p.B))[u] = C;
+  const long long a = slice_start(w, C, p.G), e = slice_start(w + 1, C, p.G);
   const long long excl = incl - own;
-  // every sequence has at least one unit, so t0 < T lies in exactly one non-empty lane range
-  const unsigned long long hit = __builtin_amdgcn_ballot_w64(own > 0 && excl <= t0 && t0 < incl);
-  const int hl = hit != 0 ? (int)__builtin_ctzll(hit) : 0;
-  long long P = readlane_ll(excl, hl);
+  // every sequence costs at least one unit, so a < C lies in exactly one non-empty lane range
+  const unsigned long long hit = __builtin_amdgcn_ballot_w64(own > 0 && excl <= a && a < incl);
+  if (hit == 0) return;  // past the last sequence
+  const int hl = (int)__builtin_ctzll(hit);
+  long long S = readlane_ll(excl, hl);
   int b = hl * kper;
   while (b + 1 < p.B) {
-    const int nb = group_units<UK>(p, b, g, window);
-    if (t0 < P + nb) break;
-    P += nb;
+    const long long cb = fixed_cost(b) + (long long)unit_cost(b) * group_units<UK>(p, b, g, window);
+    if (a < S + cb) break;
+    S += cb;
     ++b;
   }
 
   // ---- segments of this slice ----
-  long long cur = t0;
-  while (cur < t1 && b < p.B) {
+  // The merge reads the slots of slices [first, last] of each sequence: every slice in that
+  // range runs a segment of the sequence, an empty one (it writes O = 0, LSE = -inf) when no
+  // unit's position falls inside the slice.
+  while (b < p.B) {
     const int nb = group_units<UK>(p, b, g, window);
-    const long long seg_end = min(t1, P + nb);
-    SegmentCtx sg;
-    sg.b = b;
-    sg.u0 = (int)(cur - P);
-    sg.u1 = (int)(seg_end - P);
-    sg.single = (sg.u0 == 0 && sg.u1 == nb);
-    sg.slot = w + b;
-    if (meta_u != nullptr && sg.u0 == 0 && tid == 0) {
-      meta_u[2 * b] = w;
-      meta_u[2 * b + 1] = slice_of_unit(P + nb - 1, T, p.G);
+    const int cu = unit_cost(b);
+    const long long first = S + fixed_cost(b), last = first + (long long)cu * (nb - 1);
+    if (first >= e) break;
+    if (last >= a) {
+      const int u0 = a <= first ? 0 : (int)((a - first + cu - 1) / cu);
+      const int u1 = max(u0, min(nb, (int)((e - first + cu - 1) / cu)));
+      SegmentCtx sg;
+      sg.b = b;
+      sg.u0 = u0;
+      sg.u1 = u1;
+      sg.single = (u0 == 0 && u1 == nb);
+      sg.slot = w + b;
+      if (meta_u != nullptr && u0 == 0 && tid == 0) {
+        meta_u[2 * b] = w;
+        meta_u[2 * b + 1] = slice_of_unit(last, C, p.G);
+      }
+      seg(sg, g, mt);
     }
-    seg(sg, g, mt);
-    cur = seg_end;
-    P += nb;
+    S += fixed_cost(b) + (long long)cu * nb;
     ++b;
   }
 }
@@ -2273,18 +2290,15 @@ __device__ __forceinline__ bool merge_out_row(const CombineParams& p, int b, int
   return true;
 }
 
-// The slices [w0, w1] holding partials of row `row` of sequence b, and the
-// total units T of the partition they come from: that of the workgroup row
-// (query group, row tile) the row belongs to.
-__device__ __forceinline__ void merge_slices(const CombineParams& p, int b, int row, int& w0, int& w1,
-                                             long long& T) {
+// The slices [w0, w1] holding partials of row `row` of sequence b: those of the
+// workgroup row (query group, row tile) the row belongs to.
+__device__ __forceinline__ void merge_slices(const CombineParams& p, int b, int row, int& w0, int& w1) {
   const int t = row / p.H, h = row - t * p.H;
   const int g = t / p.F, f = t - g * p.F;
   const int u = ((f * p.H + h) / kTileM) * p.q_len_eff + g;
   const int32_t* m = p.meta + 2 * ((size_t)u * p.B + b);
   w0 = max(m[0], 0);
   w1 = min(m[1], p.G - 1);
-  T = ((const long long*)(p.meta + 2 * (size_t)p.U * p.B))[u];
 }
 
 // ---------------------------------------------------------------------------
@@ -2304,14 +2318,10 @@ __global__ void __launch_bounds__(256) mla_combine(CombineParams p) {
   size_t orow;
   if (!merge_out_row(p, b, row, orow)) return;
   int w0, w1;
-  long long T;
-  merge_slices(p, b, row, w0, w1, T);
+  merge_slices(p, b, row, w0, w1);
   if (w0 >= w1) return;  // single slice: written by the partial kernel
-  // slices that hold no work (more slices than units) wrote nothing: weight 0
-  auto lse_of = [&](int s) -> float {
-    if (T < p.G && slice_start(s, T, p.G) == slice_start(s + 1, T, p.G)) return -INFINITY;
-    return p.part_lse[(size_t)(s + b) * p.rows_per_b + row];
-  };
+  // (a slice without units of the sequence ran an empty segment: LSE -inf, O = 0)
+  auto lse_of = [&](int s) -> float { return p.part_lse[(size_t)(s + b) * p.rows_per_b + row]; };
   const int n = w1 - w0 + 1;
   // LSE over the slices (each thread keeps the lse values of its slices)
   float my[4];
@@ -2398,14 +2408,11 @@ __global__ void __launch_bounds__(256) mla_combine_wide(CombineParams p) {
   size_t orow;
   if (!merge_out_row(p, b, row, orow)) return;
   int w0, w1;
-  long long T;
-  merge_slices(p, b, row, w0, w1, T);
+  merge_slices(p, b, row, w0, w1);
   if (w0 >= w1) return;  // single slice: written by the partial kernel
   const int n = w1 - w0 + 1;
-  auto lse_of = [&](int s) -> float {
-    if (T < p.G && slice_start(s, T, p.G) == slice_start(s + 1, T, p.G)) return -INFINITY;
-    return p.part_lse[(size_t)(s + b) * p.rows_per_b + row];
-  };
+  // (a slice without units of the sequence ran an empty segment: LSE -inf, O = 0)
+  auto lse_of = [&](int s) -> float { return p.part_lse[(size_t)(s + b) * p.rows_per_b + row]; };
   float mx = -INFINITY;
   for (int i = lane; i < n; i += 64) mx = fmaxf(mx, lse_of(w0 + i));
   mx = wave_max(mx);
@@ -2500,14 +2507,11 @@ __global__ void __launch_bounds__(256) mla_combine_rows(CombineParams p) {
   size_t orow;
   if (!merge_out_row(p, b, row, orow)) return;
   int w0, w1;
-  long long T;
-  merge_slices(p, b, row, w0, w1, T);
+  merge_slices(p, b, row, w0, w1);
   if (w0 >= w1) return;  // single slice: written by the partial kernel
   const int n = w1 - w0 + 1;
-  auto lse_of = [&](int s) -> float {
-    if (T < p.G && slice_start(s, T, p.G) == slice_start(s + 1, T, p.G)) return -INFINITY;
-    return p.part_lse[(size_t)(s + b) * p.rows_per_b + row];
-  };
+  // (a slice without units of the sequence ran an empty segment: LSE -inf, O = 0)
+  auto lse_of = [&](int s) -> float { return p.part_lse[(size_t)(s + b) * p.rows_per_b + row]; };
   float mx = -INFINITY;
   for (int i = lane; i < n; i += 64) mx = fmaxf(mx, lse_of(w0 + i));
   mx = wave_max(mx);
@@ -2652,8 +2656,15 @@ void launch_partial_16(const PartialParams& p, bool fast_pages, bool win, dim3 g
   else launch_partial_dt<DT, false>(p, fast_pages, win, grid, block, stream);
 }
 
-hipError_t launch_partial(const PartialParams& p, int dtype, bool fast_pages, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.G * p.U)), block(kThreads);
+hipError_t launch_partial(const PartialParams& p_in, int dtype, bool fast_pages, hipStream_t stream) {
+  const dim3 grid((unsigned)(p_in.G * p_in.U)), block(kThreads);
+  // Cost model of the work partition (quarter tiles).  A segment's fixed work is worth about six
+  // 64-key E4M3 tiles (Q load, pipeline fill, partial epilogue) or four 32-key 16-bit units; a tile
+  // with the second P term costs about 1.25 tiles in the twelve-wave kernel.
+  PartialParams p = p_in;
+  const bool roles = dtype == kFp8 && (p.kernel == 0 ? kDefaultFp8Kernel : p.kernel) == 2;
+  p.seg_cost = dtype == kFp8 ? 24 : dtype == kMixed ? 12 : 16;
+  p.lo_cost = roles ? 5 : 4;
   // kernels without a sliding window are separate instantiations, so the
   // window's per-row state costs them no registers
   const bool win = p.window > 0;
