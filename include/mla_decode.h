@@ -161,8 +161,13 @@ typedef struct mla_options {
                            tests; the convention is this library's reading.)  < 0:
                            MLA_ERR_SHAPE.  Plan the workspace with the same options. */
   int32_t kernel;       /* E4M3 inputs: 1 the four-wave split-KV kernel, 2 the twelve-wave
-                           role-specialised one (the default, 0); other dtypes ignore it.
-                           Other values: MLA_ERR_SHAPE */
+                           role-specialised one; 0 the default: the four-wave kernel when
+                           page_size is at least 64 (whole 64-key tiles per page) and no window
+                           is set, the twelve-wave kernel otherwise.  Sequences of at most 8,192 keys take a second P
+                           term (E2M1 codes of E4M3's rounding residual) in the twelve-wave
+                           kernel and in the default four-wave one; a four-wave kernel forced
+                           onto other pages or a window runs without it.  Other dtypes ignore
+                           the field.  Other values: MLA_ERR_SHAPE */
   int32_t merge;        /* rows merged from many slices: 0 the wide merge (a wave per quarter row,
                            a whole chunk of slices in flight; the default), 1 a workgroup per row
                            (kept for comparison).  Other values: MLA_ERR_SHAPE */

@@ -409,8 +409,15 @@ __device__ __forceinline__ int group_units(const PartialParams& p, int b, int g,
   return units_of<UK>(n_gmax - seq_key0<UK>(L, qlen_b, window));
 }
 
+// Sequences of at most this many keys take the second P term.  The E4M3 rounding of P moves a
+// row's output by up to ~2^-4 of the weight its few largest keys carry; over many keys the
+// weights spread and the per-key errors average out (on the ragged speculative-decoding
+// workload the single-term error falls from 5e-2 at 1-2K keys to 2e-2 above 8K).
+constexpr int kLoKeys = 8192;
+
 // XPV (16-bit paths): the fp8 path's cross-wave PV layout instead of the own-rows one.
-template <int DT, bool FAST, bool WIN, bool XPV>
+// LO (E4M3): P goes out in two terms, E4M3 codes and E2M1 codes of their rounding residuals.
+template <int DT, bool FAST, bool WIN, bool XPV, bool LO = false>
 __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem, int* s_flag, const SegmentCtx& sg,
                                             int g, int mt, int wave, int lane) {
   using TR = Traits<DT>;
@@ -752,6 +759,9 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         v16f s0, s1;            // scores of the tile passing through the score MFMAs
         v16f hb;                // keys 32..63 of the previous tile's scores
         int pa[4], pb[4];       // fp8 P words: keys 0..31 and 32..63
+        // (LO) E2M1 codes of half the E4M3 rounding residual of each P element: nibble k of
+        // la / lb belongs to byte k of pa / pb
+        int la[2] = {0, 0}, lb[2] = {0, 0};
         float pe_off = 0.f;     // exp2 offset of the tile whose P is being built
         int pe_e = 0;           // its power-of-two scale
         float lsum = 0.f, lsum_r = 0.f, mx_raw = -INFINITY, p_hold = 0.f;
@@ -774,7 +784,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         // Returns the sum of the two values as rounded to E4M3: O is normalised by the sum of
         // the weights the PV product used, so they sum to one (a row that sees one key returns
         // that key's V exactly); the LSE keeps the exact sum.
-        auto pack_pair = [&](float p0, float p1, int pair, int* words) -> float {
+        auto pack_pair = [&](float p0, float p1, int pair, int* words, int* lo) -> float {
           // pair j holds elements 2j, 2j+1: even pairs fill the low half of word j/2, odd pairs the high
           v2f r;
           if ((pair & 1) == 0) {
@@ -785,6 +795,20 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             words[pair >> 1] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, w_hold, true);
             fence_v(words[pair >> 1]);
             r = __builtin_amdgcn_cvt_pk_f32_fp8(words[pair >> 1], true);
+          }
+          if constexpr (LO) {
+            // the residuals as E2M1 codes of half their value (every p is at most 256 here, so a
+            // residual is at most 8) into byte pair % 4 of lo word pair / 4 (byte selects must be
+            // literal constants)
+            const float d0 = p0 - r[0], d1 = p1 - r[1];
+            uint32_t lw = (uint32_t)lo[pair >> 2];
+            switch (pair & 3) {
+              case 0: lw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lw, d0, d1, 2.f, 0); break;
+              case 1: lw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lw, d0, d1, 2.f, 1); break;
+              case 2: lw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lw, d0, d1, 2.f, 2); break;
+              default: lw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lw, d0, d1, 2.f, 3); break;
+            }
+            lo[pair >> 2] = (int)lw;
           }
           return r[0] + r[1];
         };
@@ -841,7 +865,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             if (t >= 2) {
               const int j = t - 2;
               lsum += qa[j & 1] + qb[j & 1];
-              lsum_r += pack_pair(qa[j & 1], qb[j & 1], j, pa);
+              lsum_r += pack_pair(qa[j & 1], qb[j & 1], j, pa, la);
               fence_v(lsum);
               fence_v(lsum_r);
             }
@@ -872,7 +896,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
               p_hold = qa[k & 1];
               fence_v(p_hold);
             } else {
-              lsum_r += pack_pair(p_hold, qa[k & 1], k >> 1, pb);
+              lsum_r += pack_pair(p_hold, qa[k & 1], k >> 1, pb, lb);
               fence_v(lsum_r);
             }
           }
@@ -924,11 +948,17 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           }
         };
         // this wave's P (its 32 rows, B-operand layout) and per-row scale into LDS
-        auto p_publish = [&]() {
+        // (LO) The second term of a tile's P goes into the rope columns of the tile's own stage
+        // (bytes 512..575 of its 64 rows): every wave is past the tile's scores, and the stage is
+        // not reloaded before the tile's PV.  Entry 64 w + lane (16 bytes) sits at row entry / 4,
+        // bytes 512 + 16 (entry % 4).
+        auto lo_entry = [&](const lds_t* st, int e) -> const lds_t* { return st + (e >> 2) * RB + 512 + 16 * (e & 3); };
+        auto p_publish = [&](const lds_t* st) {
           lds_t* pw = smem + kPOffset + wave * 2048;
           *(lds_v4i*)(pw + 16 * lane) = v4i{pa[0], pa[1], pa[2], pa[3]};
           *(lds_v4i*)(pw + 1024 + 16 * lane) = v4i{pb[0], pb[1], pb[2], pb[3]};
           *(__attribute__((address_space(3))) int*)(smem + kPScaleOffset + 256 * wave + 4 * lane) = 127 - pe_e;
+          if constexpr (LO) *(lds_v4i*)lo_entry(st, 64 * wave + lane) = v4i{la[0], la[1], lb[0], lb[1]};
         };
         // O^T += V^T P^T for this wave's 128 latent dims (4 blocks of 32) and all
         // four row blocks: each transposed V read feeds four MFMAs.  Accumulator
@@ -983,6 +1013,35 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             if (k == 7) vb[1] = vread(st, 4 * wave + 3);
             __builtin_amdgcn_sched_barrier(0);
           }
+          if constexpr (LO) {
+            // The residual term: B in E2M1 (blgp 4) at twice the E4M3 term's scale, latent blocks
+            // 2 and 3 (in vb) and then 0 and 1, each row block's operand read where it is used.
+            // The E2M1 operand of a column: lane half h takes bytes 8h..8h+7 of the entries of
+            // lanes n and n + 32 (its K-slots are those of E4M3 bytes 16h..16h+15 of both halves).
+            const int hb = 8 * (lane >> 5), ln = lane & 31;
+#pragma unroll
+            for (int jp = 0; jp < 2; ++jp) {
+              const int j0 = jp == 0 ? 2 : 0;
+              if (jp == 1) {
+                vb[0] = vread(st, 4 * wave);
+                vb[1] = vread(st, 4 * wave + 1);
+              }
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                const int r = (wave + rr) & 3;
+                const v2i l0 = *(const lds_v2i*)(lo_entry(st, 64 * r + ln) + hb);
+                const v2i l1 = *(const lds_v2i*)(lo_entry(st, 64 * r + 32 + ln) + hb);
+                const v8i pl = v8i{l0[0], l0[1], l1[0], l1[1], 0, 0, 0, 0};
+                o[4 * j0 + rr] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vb[0], pl, o[4 * j0 + rr], 0, 4, 0,
+                                                                                127, 0, psc[rr] + 1);
+                o[4 * j0 + 4 + rr] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    vb[1], pl, o[4 * j0 + 4 + rr], 0, 4, 0, 127, 0, psc[rr] + 1);
+                pin_agpr(o[4 * j0 + rr]);
+                pin_agpr(o[4 * j0 + 4 + rr]);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
         };
 
         // Q: each wave's 32 rows (18 KiB, one contiguous block of the folded
@@ -1035,7 +1094,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           dma_setup(t + 2);
           hb = s1;
           qk_chain(stage(t), true);  // also finishes the softmax of tile t-1
-          p_publish();
+          p_publish(stage(t - 1));
           pv_prefetch(stage(t - 1));
           lds_barrier();  // P of tile t-1 from all waves is visible
           const int key0 = k0 + t * TILE;
@@ -1044,7 +1103,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         hb = s1;
 #pragma unroll
         for (int slot = 0; slot < 18; ++slot) part_b(slot);
-        p_publish();
+        p_publish(stage(ntiles - 1));
         pv_prefetch(stage(ntiles - 1));
         lds_barrier();
         pv_chain(stage(ntiles - 1), false, 0, false);
@@ -1338,8 +1397,9 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
     const float l_tot = xor32_sum(l_acc);
     const bool has = l_tot > 0.f;
     // O is normalised by the sum of the weights the PV product used (P as rounded to its
-    // operand type), the LSE by the exact sum
-    const float l_norm = xor32_sum(DT == kFp8 ? l_acc_r : *lr_slot());
+    // operand type), the LSE by the exact sum; with the second E4M3 term the weights are P up to
+    // E2M1's rounding of the residual, and the exact sum normalises O as well
+    const float l_norm = DT == kFp8 ? (LO ? l_tot : xor32_sum(l_acc_r)) : xor32_sum(*lr_slot());
     const float inv = has && l_norm > 0.f ? p.v_scale / l_norm : 0.f;
     const float lse_v = has ? (m_ref + log2f(l_tot)) * kLn2 : -INFINITY;
     lds_f32* s_inv = (lds_f32*)(smem + kPOffset);
@@ -1531,11 +1591,6 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
 // waves scale the row's output accumulators by it before adding the tile.
 // ---------------------------------------------------------------------------
 constexpr int kThreadsR = 768;
-// Sequences of at most this many keys take the second P term.  The E4M3 rounding of P moves a
-// row's output by up to ~2^-4 of the weight its few largest keys carry; over many keys the
-// weights spread and the per-key errors average out (on the ragged speculative-decoding
-// workload the single-term error falls from 5e-2 at 1-2K keys to 2e-2 above 8K).
-constexpr int kLoKeys = 8192;
 constexpr int kRDummy = kStages * kStageBytes;  // 1 KiB: destination of dummy-tile loads
 constexpr int kRP = kRDummy + 1024;              // P codes: [row block 4][half 2][lane 64][16 bytes]
 constexpr int kRScale = kRP + 8192;              // E8M0 scale codes: [row block 4][lane 64] int32
@@ -2251,7 +2306,16 @@ mla_split_kv_partial(PartialParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases in SGPRs
   for_each_segment<Traits<DT>::kTile, WIN>(p, tid, lane, [&](const SegmentCtx& sg, int g, int mt) {
-    run_segment<DT, FAST, WIN, XPV>(p, smem, s_flag, sg, g, mt, wave, lane);
+    if constexpr (DT == kFp8 && FAST && !WIN) {
+      // two copies of the segment code, so that the second P term costs the long sequences nothing
+      if (((cint_t*)p.seq_lens)[sg.b] <= kLoKeys) {
+        run_segment<DT, FAST, WIN, XPV, true>(p, smem, s_flag, sg, g, mt, wave, lane);
+      } else {
+        run_segment<DT, FAST, WIN, XPV, false>(p, smem, s_flag, sg, g, mt, wave, lane);
+      }
+    } else {
+      run_segment<DT, FAST, WIN, XPV>(p, smem, s_flag, sg, g, mt, wave, lane);
+    }
   });
 }
 
@@ -2662,15 +2726,18 @@ hipError_t launch_partial(const PartialParams& p_in, int dtype, bool fast_pages,
   // 64-key E4M3 tiles (Q load, pipeline fill, partial epilogue) or four 32-key 16-bit units; a tile
   // with the second P term costs about 1.25 tiles in the twelve-wave kernel.
   PartialParams p = p_in;
-  const bool roles = dtype == kFp8 && (p.kernel == 0 ? kDefaultFp8Kernel : p.kernel) == 2;
-  p.seg_cost = dtype == kFp8 ? 24 : dtype == kMixed ? 12 : 16;
-  p.lo_cost = roles ? 5 : 4;
   // kernels without a sliding window are separate instantiations, so the
   // window's per-row state costs them no registers
   const bool win = p.window > 0;
+  // E4M3 default: the four-wave kernel on whole-tile pages without a window (the instantiation with
+  // the second P term), the twelve-wave kernel elsewhere
+  const int fp8_kernel = p.kernel != 0 ? p.kernel : (fast_pages && !win ? 1 : 2);
+  const bool lo_terms = dtype == kFp8 && (fp8_kernel == 2 || (fast_pages && !win));
+  p.seg_cost = dtype == kFp8 ? 24 : dtype == kMixed ? 12 : 16;
+  p.lo_cost = !lo_terms ? 4 : fp8_kernel == 2 ? 5 : 6;
   switch (dtype) {
     case kFp8:
-      if ((p.kernel == 0 ? kDefaultFp8Kernel : p.kernel) == 1) {
+      if (fp8_kernel == 1) {
         launch_partial_dt<kFp8, true>(p, fast_pages, win, grid, block, stream);  // the four-wave kernel
       } else if (fast_pages) {
         launch_fp8_roles<true>(p, win, grid, stream);
