@@ -45,10 +45,9 @@ struct PartialParams {
   const int32_t* cu_q;       // ragged batch: [B+1] cumulative new-token counts (device), or nullptr
   int32_t total_q;           // ragged batch: token rows of q / out
   int32_t kernel;            // E4M3: 1 the four-wave kernel, 2 the role-specialised kernel, 0 the default (see launch_partial)
-  // Work partition in cost units of a quarter tile: a (sequence, query group) pair costs seg_cost
-  // (the fixed work of a segment) plus 4 per tile, or lo_cost per tile for E4M3 sequences that take
-  // the second P term (set per kernel at launch)
-  int32_t seg_cost, lo_cost;
+  // Work partition in cost units of a quarter tile: a tile costs 4, or lo_cost in E4M3 sequences
+  // that take the second P term (set per kernel at launch)
+  int32_t lo_cost;
 };
 
 struct CombineParams {

@@ -365,6 +365,7 @@ __device__ __forceinline__ int slice_of_unit(long long u, long long T, int G) {
 struct SegmentCtx {
   int b, u0, u1, slot;
   bool single;
+  int L, qlen, tok0;  // sequence b: keys (clamped at 0), new tokens, first token row (seq_tokens)
 };
 
 // ---------------------------------------------------------------------------
@@ -399,12 +400,9 @@ __device__ __forceinline__ void seq_tokens(const PartialParams& p, int b, int& q
 // sequence (a ragged batch's shorter sequences) keeps one empty unit, so every
 // (group, sequence) pair has at least one.
 template <int UK>
-__device__ __forceinline__ int group_units(const PartialParams& p, int b, int g, int window) {
-  int qlen_b, tok0;
-  seq_tokens(p, b, qlen_b, tok0);
+__device__ __forceinline__ int group_units_of(const PartialParams& p, int L, int qlen_b, int g, int window) {
   const int gF = g * p.F;
   if (qlen_b <= gF) return 1;
-  const int L = max(((cint_t*)p.seq_lens)[b], 0);
   const int n_gmax = min(max(L - qlen_b + gF + p.F, 0), L);
   return units_of<UK>(n_gmax - seq_key0<UK>(L, qlen_b, window));
 }
@@ -433,10 +431,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   asm volatile("" : "+s"(wave));
   const int n = lane & 31;
   const int hh = lane >> 5;
-  cint_t* seq_lens = (cint_t*)p.seq_lens;
-  const int L = max(seq_lens[sg.b], 0);
-  int qlen_b, tok0;
-  seq_tokens(p, sg.b, qlen_b, tok0);
+  const int L = sg.L, qlen_b = sg.qlen, tok0 = sg.tok0;
   const int gF = g * p.F;
   // folded rows that hold a token of this sequence (fewer than H_eff only in the
   // last query group of a ragged batch's shorter sequences; none past its end)
@@ -1620,10 +1615,7 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
   const int pw = wave - 4;                         // PV role: latent dims [64 pw, +64)
   const bool dma_wave = !SCORE && wave < 8;        // issue the tile loads (PV waves 4-7)
   const int dw = wave - 4;                         // their index
-  cint_t* seq_lens = (cint_t*)p.seq_lens;
-  const int L = max(seq_lens[sg.b], 0);
-  int qlen_b, tok0;
-  seq_tokens(p, sg.b, qlen_b, tok0);
+  const int L = sg.L, qlen_b = sg.qlen, tok0 = sg.tok0;
   const int gF = g * p.F;
   const int rows_valid = min(p.H_eff, max(qlen_b - gF, 0) * p.H);
   if (rows_valid <= mt * kTileM) return;
@@ -2200,7 +2192,8 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
 // total work T and the slice's first sequence, records the merge metadata, and
 // calls seg(sg, g, mt) for each (slice, sequence) segment in order.  Uniform
 // across the workgroup (every wave computes the same answer).
-template <int UK, bool WIN, typename SegFn>
+// KEEP: lanes keep the sequences' values across the segments (kernels with registers to spare).
+template <int UK, bool WIN, bool KEEP, typename SegFn>
 __device__ __forceinline__ void for_each_segment(const PartialParams& p, int tid, int lane, SegFn&& seg) {
   int w, u;
   if (p.xcd_map) {
@@ -2232,23 +2225,46 @@ __device__ __forceinline__ void for_each_segment(const PartialParams& p, int tid
 
   // ---- the row's work in cost units, and the slice's first sequence ----
   // Sequence b of this row holds n_b units (tiles).  It costs c_b per unit: 4, or p.lo_cost for
-  // an E4M3 sequence that takes the second P term; every sequence but the first also costs
-  // p.seg_cost, the fixed work (Q load, pipeline fill, epilogue) of the extra segment its start
-  // adds to the slice it starts in.  The slices cut the row's total cost C evenly, and unit i of b
-  // belongs to the slice holding its position S_b + z_b + c_b i (S_b: the cost of the sequences
-  // before b, z_b its fixed cost), so slices full of costlier units or of short sequences get fewer.
+  // an E4M3 sequence that takes the second P term.  The slices cut the row's total cost C evenly,
+  // and unit i of b belongs to the slice holding its position S_b + c_b i (S_b: the cost of the
+  // sequences before b), so slices full of costlier units get fewer of them.
   // Every wave computes the same answer on its own (no LDS, no barrier): lane i sums the costs of
   // sequences [i*kper, (i+1)*kper), one wave-wide prefix sum gives C and each lane's first
   // position, and the lane whose range holds the slice's start is found by ballot.
   const int kper = (p.B + 63) >> 6;
   const int bl0 = min(lane * kper, p.B), bl1 = min(bl0 + kper, p.B);
   const int window = WIN ? p.window : 0;
-  auto unit_cost = [&](int bb) -> int {
-    return p.lo_cost != 4 && ((cint_t*)p.seq_lens)[bb] <= kLoKeys ? p.lo_cost : 4;
+  struct SeqV {
+    int L, qlen, tok0, n, c;
   };
+  auto load_seq = [&](int bb) -> SeqV {
+    SeqV v;
+    seq_tokens(p, bb, v.qlen, v.tok0);
+    v.L = max(((cint_t*)p.seq_lens)[bb], 0);
+    v.n = group_units_of<UK>(p, v.L, v.qlen, g, window);
+    v.c = p.lo_cost != 4 && v.L <= kLoKeys ? p.lo_cost : 4;
+    return v;
+  };
+  // With KEEP and at most 64 sequences lane b keeps sequence b's values, and the walks below read
+  // them with readlane instead of waiting on memory again (each dependent load costs a memory
+  // latency); kernels without registers to spare do not keep them.
+  SeqV mine = {0, 0, 0, 0, 4};
   long long own = 0;
-  auto fixed_cost = [&](int bb) -> int { return bb > 0 ? p.seg_cost : 0; };
-  for (int bb = bl0; bb < bl1; ++bb) own += fixed_cost(bb) + (long long)unit_cost(bb) * group_units<UK>(p, bb, g, window);
+  for (int bb = bl0; bb < bl1; ++bb) {
+    const SeqV v = load_seq(bb);
+    own += (long long)v.c * v.n;
+    mine = v;
+  }
+  auto seq_of = [&](int bb) -> SeqV {
+    if (!KEEP || kper != 1) return load_seq(bb);
+    SeqV v;
+    v.L = __builtin_amdgcn_readlane(mine.L, bb);
+    v.qlen = __builtin_amdgcn_readlane(mine.qlen, bb);
+    v.tok0 = __builtin_amdgcn_readlane(mine.tok0, bb);
+    v.n = __builtin_amdgcn_readlane(mine.n, bb);
+    v.c = __builtin_amdgcn_readlane(mine.c, bb);
+    return v;
+  };
   const long long incl = wave_incl_scan_ll(own);
   const long long C = readlane_ll(incl, 63);
   int32_t* meta_u = p.meta != nullptr ? p.meta + 2 * (size_t)u * p.B : nullptr;
@@ -2262,7 +2278,8 @@ __device__ __forceinline__ void for_each_segment(const PartialParams& p, int tid
   long long S = readlane_ll(excl, hl);
   int b = hl * kper;
   while (b + 1 < p.B) {
-    const long long cb = fixed_cost(b) + (long long)unit_cost(b) * group_units<UK>(p, b, g, window);
+    const SeqV v = seq_of(b);
+    const long long cb = (long long)v.c * v.n;
     if (a < S + cb) break;
     S += cb;
     ++b;
@@ -2273,9 +2290,9 @@ __device__ __forceinline__ void for_each_segment(const PartialParams& p, int tid
   // range runs a segment of the sequence, an empty one (it writes O = 0, LSE = -inf) when no
   // unit's position falls inside the slice.
   while (b < p.B) {
-    const int nb = group_units<UK>(p, b, g, window);
-    const int cu = unit_cost(b);
-    const long long first = S + fixed_cost(b), last = first + (long long)cu * (nb - 1);
+    const SeqV v = seq_of(b);
+    const int nb = v.n, cu = v.c;
+    const long long first = S, last = first + (long long)cu * (nb - 1);
     if (first >= e) break;
     if (last >= a) {
       const int u0 = a <= first ? 0 : (int)((a - first + cu - 1) / cu);
@@ -2286,13 +2303,16 @@ __device__ __forceinline__ void for_each_segment(const PartialParams& p, int tid
       sg.u1 = u1;
       sg.single = (u0 == 0 && u1 == nb);
       sg.slot = w + b;
+      sg.L = v.L;
+      sg.qlen = v.qlen;
+      sg.tok0 = v.tok0;
       if (meta_u != nullptr && u0 == 0 && tid == 0) {
         meta_u[2 * b] = w;
         meta_u[2 * b + 1] = slice_of_unit(last, C, p.G);
       }
       seg(sg, g, mt);
     }
-    S += fixed_cost(b) + (long long)cu * nb;
+    S += (long long)cu * nb;
     ++b;
   }
 }
@@ -2305,10 +2325,12 @@ mla_split_kv_partial(PartialParams p) {
   lds_t* smem = (lds_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases in SGPRs
-  for_each_segment<Traits<DT>::kTile, WIN>(p, tid, lane, [&](const SegmentCtx& sg, int g, int mt) {
+  // (the E4M3 instantiations forced onto short pages or a window have no register to keep them in)
+  constexpr bool kKeep = DT != kFp8 || (FAST && !WIN);
+  for_each_segment<Traits<DT>::kTile, WIN, kKeep>(p, tid, lane, [&](const SegmentCtx& sg, int g, int mt) {
     if constexpr (DT == kFp8 && FAST && !WIN) {
       // two copies of the segment code, so that the second P term costs the long sequences nothing
-      if (((cint_t*)p.seq_lens)[sg.b] <= kLoKeys) {
+      if (sg.L <= kLoKeys) {
         run_segment<DT, FAST, WIN, XPV, true>(p, smem, s_flag, sg, g, mt, wave, lane);
       } else {
         run_segment<DT, FAST, WIN, XPV, false>(p, smem, s_flag, sg, g, mt, wave, lane);
@@ -2328,11 +2350,11 @@ mla_split_kv_fp8_roles(PartialParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // two instantiations in separate branches: a wave's registers hold only its role's state
   if (wave < 4) {
-    for_each_segment<64, WIN>(p, tid, lane, [&](const SegmentCtx& sg, int g, int mt) {
+    for_each_segment<64, WIN, false>(p, tid, lane, [&](const SegmentCtx& sg, int g, int mt) {
       run_segment_roles<FAST, WIN, true>(p, smem, sg, g, mt, wave, lane);
     });
   } else {
-    for_each_segment<64, WIN>(p, tid, lane, [&](const SegmentCtx& sg, int g, int mt) {
+    for_each_segment<64, WIN, false>(p, tid, lane, [&](const SegmentCtx& sg, int g, int mt) {
       run_segment_roles<FAST, WIN, false>(p, smem, sg, g, mt, wave, lane);
     });
   }
@@ -2722,9 +2744,8 @@ void launch_partial_16(const PartialParams& p, bool fast_pages, bool win, dim3 g
 
 hipError_t launch_partial(const PartialParams& p_in, int dtype, bool fast_pages, hipStream_t stream) {
   const dim3 grid((unsigned)(p_in.G * p_in.U)), block(kThreads);
-  // Cost model of the work partition (quarter tiles).  A segment's fixed work is worth about six
-  // 64-key E4M3 tiles (Q load, pipeline fill, partial epilogue) or four 32-key 16-bit units; a tile
-  // with the second P term costs about 1.25 tiles in the twelve-wave kernel.
+  // Cost model of the work partition (quarter tiles): a tile with the second P term costs about
+  // 1.25 tiles in the twelve-wave kernel and 1.5 in the four-wave one.
   PartialParams p = p_in;
   // kernels without a sliding window are separate instantiations, so the
   // window's per-row state costs them no registers
@@ -2733,7 +2754,6 @@ hipError_t launch_partial(const PartialParams& p_in, int dtype, bool fast_pages,
   // the second P term), the twelve-wave kernel elsewhere
   const int fp8_kernel = p.kernel != 0 ? p.kernel : (fast_pages && !win ? 1 : 2);
   const bool lo_terms = dtype == kFp8 && (fp8_kernel == 2 || (fast_pages && !win));
-  p.seg_cost = dtype == kFp8 ? 24 : dtype == kMixed ? 12 : 16;
   p.lo_cost = !lo_terms ? 4 : fp8_kernel == 2 ? 5 : 6;
   switch (dtype) {
     case kFp8:
