@@ -2325,8 +2325,9 @@ mla_split_kv_partial(PartialParams p) {
   lds_t* smem = (lds_t*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps LDS bases in SGPRs
-  // (the E4M3 instantiations forced onto short pages or a window have no register to keep them in)
-  constexpr bool kKeep = DT != kFp8 || (FAST && !WIN);
+  // (only the default E4M3 instantiation: the others have no register to keep them in, and in the
+  // 16-bit kernels the values held across their segments cost more than the loads they save)
+  constexpr bool kKeep = DT == kFp8 && FAST && !WIN;
   for_each_segment<Traits<DT>::kTile, WIN, kKeep>(p, tid, lane, [&](const SegmentCtx& sg, int g, int mt) {
     if constexpr (DT == kFp8 && FAST && !WIN) {
       // two copies of the segment code, so that the second P term costs the long sequences nothing
