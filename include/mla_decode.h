@@ -168,9 +168,11 @@ typedef struct mla_options {
                            kernel and in the default four-wave one; a four-wave kernel forced
                            onto other pages or a window runs without it.  Other dtypes ignore
                            the field.  Other values: MLA_ERR_SHAPE */
-  int32_t merge;        /* rows merged from many slices: 0 the wide merge (a wave per quarter row,
-                           a whole chunk of slices in flight; the default), 1 a workgroup per row
-                           (kept for comparison).  Other values: MLA_ERR_SHAPE */
+  int32_t merge;        /* rows merged from many slices (more than 16 per row on average): 0 the
+                           wide merge (a wave per quarter row, a whole chunk of slices in flight;
+                           the default), 1 a workgroup per row (kept for comparison); 2 the
+                           per-wave merge (a wave per row), which rows over at most 16 slices on
+                           average always take.  Other values: MLA_ERR_SHAPE */
   int32_t reserved[1];
   void* split_event;    /* hipEvent_t or NULL: recorded on `stream` after the split-KV kernel
                            and before the merge kernel, so callers can time each kernel */

@@ -75,8 +75,9 @@ def options(num_splits: int = 0, no_fold: bool = False, partial_fp32: bool = Fal
     stages 1 / 2 launch only the split-KV / only the merge kernel; window > 0 is the sliding-window mask
     (token t sees keys [max(0, n_t - window), n_t)); kernel 1 / 2 select the four-wave / the
     role-specialised twelve-wave E4M3 split-KV kernel (0: the default, the four-wave kernel on pages of
-    at least 64 keys without a window, the twelve-wave one otherwise); merge 1 selects the
-    workgroup-per-row merge for rows spread over many slices (0: the wide merge)."""
+    at least 64 keys without a window, the twelve-wave one otherwise); for rows spread over more than 16
+    slices on average, merge 1 selects the workgroup-per-row merge and 2 the per-wave one (0: the wide
+    merge)."""
     o = MlaOptions()
     o.num_splits = int(num_splits)
     o.no_fold = int(bool(no_fold))

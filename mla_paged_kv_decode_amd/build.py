@@ -3,7 +3,9 @@
 The library holds the host runtime (csrc/mla_api.cpp) and the HIP kernels
 (csrc/mla_kernels.hip).  The compiler's kernel-resource remarks are parsed
 into a per-kernel report (VGPRs, AGPRs, scratch, LDS, spills) printed after
-the build and kept next to the library as kernel_resources.txt.
+the build and kept next to the library as kernel_resources.txt.  The build
+fails if a kernel of the default paths spills a VGPR (spill_gate), or if the
+assembly shows an MFMA hazard or a spill inside a tile loop (asm_lint).
 """
 from __future__ import annotations
 
@@ -53,6 +55,28 @@ def parse_resources(text: str) -> dict:
     return kernels
 
 
+# Kernels that must not spill a VGPR: the split-KV instantiations the default paths run over pages
+# of at least a tile (E4M3 without a window; every 16-bit dtype and layout, with or without one),
+# the merges and the pack kernel.  The others (E4M3 with a window or over short pages in the
+# four-wave kernel, the twelve-wave kernel, 16-bit kernels over short pages) spill a few values
+# outside their tile loop, which the assembly lint keeps out of the loop itself.
+_SPLIT = re.compile(r"mla_split_kv_partialILi(\d)ELb([01])ELb([01])ELb([01])E")
+
+
+def must_not_spill(name: str) -> bool:
+    m = _SPLIT.search(name)
+    if m:
+        dt, fast, win = int(m.group(1)), m.group(2) == "1", m.group(3) == "1"
+        return fast and (dt != 2 or not win)
+    return "mla_combine" in name or "mla_kv_pack" in name
+
+
+def spill_gate(resources: dict) -> list:
+    """Names (with their VGPR spill counts) of the kernels that must not spill but do."""
+    return [f"{k}: {r.get('VGPRs Spill')} VGPRs spilled" for k, r in sorted(resources.items())
+            if must_not_spill(k) and r.get("VGPRs Spill", 0) != 0]
+
+
 def lint_assembly() -> None:
     """Compile the kernels to gfx950 assembly and check the inline-asm MFMA hazards (asm_lint)."""
     import tempfile
@@ -62,7 +86,8 @@ def lint_assembly() -> None:
 
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "mla_kernels.s")
-        cmd = [_hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "--cuda-device-only", "-S",
+        # (-fPIC as in the library build: it changes the device code's register allocation)
+        cmd = [_hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "--cuda-device-only", "-S",
                "-I", os.path.join(ROOT, "include"), "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-Wno-inline-asm", SOURCES[0], "-o", out]
         proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -87,13 +112,16 @@ def build(verbose: bool = False) -> str:
     if proc.returncode != 0:
         sys.stderr.write(proc.stdout)
         raise RuntimeError(f"hipcc failed ({proc.returncode})")
+    res = parse_resources(proc.stdout)
     try:
+        spills = spill_gate(res)
+        if spills:
+            raise RuntimeError("VGPR spills in kernels that must not spill:\n  " + "\n  ".join(spills))
         lint_assembly()
     except Exception:
         os.remove(tmp)
         raise
     os.replace(tmp, LIB)
-    res = parse_resources(proc.stdout)
     lines = []
     for name, r in sorted(res.items()):
         lines.append(

@@ -185,7 +185,7 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
   if (opt && (opt->stages < 0 || opt->stages > 2)) return fail(MLA_ERR_SHAPE, "options.stages must be 0, 1 or 2");
   if (opt && opt->window < 0) return fail(MLA_ERR_SHAPE, "options.window must be >= 0 (got %d)", opt->window);
   if (opt && (opt->kernel < 0 || opt->kernel > 2)) return fail(MLA_ERR_SHAPE, "options.kernel must be 0, 1 or 2");
-  if (opt && (opt->merge < 0 || opt->merge > 1)) return fail(MLA_ERR_SHAPE, "options.merge must be 0 or 1");
+  if (opt && (opt->merge < 0 || opt->merge > 2)) return fail(MLA_ERR_SHAPE, "options.merge must be 0, 1 or 2");
   if (!s) return fail(MLA_ERR_NULL, "shape is NULL");
   if (s->dtype != MLA_DTYPE_BF16 && s->dtype != MLA_DTYPE_FP8_E4M3 && s->dtype != MLA_DTYPE_FP16 &&
       s->dtype != MLA_DTYPE_BF16_Q_FP8_KV)

@@ -62,7 +62,7 @@ struct CombineParams {
   int32_t F, q_len_eff, U;    // fold factor, query groups, workgroup rows (meta is [U][B][2], then int64 T[U])
   const int32_t* cu_q;        // ragged batch: [B+1] cumulative new-token counts, or nullptr
   int32_t total_q;
-  int32_t merge_kernel;       // rows over many slices: 0 the wide merge (a wave per row quarter), 1 a workgroup per row
+  int32_t merge_kernel;       // rows over many slices: 0 the wide merge (a wave per row quarter), 1 a workgroup per row, 2 a wave per row
 };
 
 struct PackParams {
@@ -77,9 +77,10 @@ struct PackParams {
 
 // Launchers (defined in mla_kernels.hip).  Return the launch's hipError_t.
 hipError_t launch_partial(const PartialParams& p, int dtype, bool fast_pages, hipStream_t stream);
-// The merge runs one wave per output row when sequences span few slices on
-// average (G < 16 B), and one workgroup per row otherwise.
-inline bool combine_per_wave(int B, int G) { return (long long)G < 16LL * B; }
+// The merge runs one wave per output row when sequences span at most 16 slices
+// on average (G <= 16 B: one chunk of the per-wave merge's loads), and spreads a
+// row over a workgroup otherwise.
+inline bool combine_per_wave(int B, int G) { return (long long)G <= 16LL * B; }
 // The 16-bit kernels spread PV over all four waves (the fp8 layout: P through
 // LDS, one more barrier per 32 keys) when a workgroup's 128 rows are not all
 // filled, i.e. fewer than 128 folded rows: otherwise the waves holding rows

@@ -243,6 +243,15 @@ __device__ __forceinline__ float xor32_sum(float x) {
 // gets a VGPR copy.
 __device__ __forceinline__ void pin_agpr(v16f& x) { asm volatile("" : "+a"(x)); }
 
+// This lane's index (0..63), recomputed where it is used: an opaque instruction pair that the
+// compiler cannot hoist, so no register holds the lane id across a segment loop (in the kernels
+// that use all 512 registers such a value spills).
+__device__ __forceinline__ int lane_id_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // Work units of the KV partition are one LDS tile of the kernel: UK = 64 keys
 // (E4M3 tiles) or 32 (16-bit tiles).  A sequence has at least one unit.
 template <int UK>
@@ -258,15 +267,41 @@ __device__ __forceinline__ int seq_key0(int L, int q_len, int window) {
   return lo > 0 ? (int)(lo & ~(long long)(UK - 1)) : 0;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
+// Butterfly reduction over the 64 lanes with no lane-index registers: v_permlane32_swap pairs
+// lane i with lane i ^ 32, then ds_swizzle in bit-mask mode (and-mask 31, xor-mask k) pairs each
+// lane with lane i ^ k inside its half, for k = 16, 8, 4, 2, 1.  Every lane ends with the result.
+// (A shuffle by lane index would keep six loop-invariant index registers live, and spill them.)
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  int x = __builtin_bit_cast(int, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);  // {own, partner} in some order
+  v = op(__builtin_bit_cast(T, (int)r[0]), __builtin_bit_cast(T, (int)r[1]));
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  for (int k = 16; k > 0; k >>= 1) {
+    x = __builtin_bit_cast(int, v);
+    int y;
+    switch (k) {  // the swizzle pattern is an immediate
+      case 16: y = __builtin_amdgcn_ds_swizzle(x, (16 << 10) | 31); break;
+      case 8: y = __builtin_amdgcn_ds_swizzle(x, (8 << 10) | 31); break;
+      case 4: y = __builtin_amdgcn_ds_swizzle(x, (4 << 10) | 31); break;
+      case 2: y = __builtin_amdgcn_ds_swizzle(x, (2 << 10) | 31); break;
+      default: y = __builtin_amdgcn_ds_swizzle(x, (1 << 10) | 31); break;
+    }
+    v = op(v, __builtin_bit_cast(T, y));
+  }
   return v;
 }
+__device__ __forceinline__ float wave_max(float v) {
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return wave_reduce(v, [](float a, float b) { return a + b; });
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+  return wave_reduce(v, [](int a, int b) { return min(a, b); });
+}
+__device__ __forceinline__ int wave_max_i32(int v) {
+  return wave_reduce(v, [](int a, int b) { return max(a, b); });
 }
 // Inclusive prefix sum over the 64 lanes of a wave, on DPP moves (no LDS
 // traffic): shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then the
@@ -448,7 +483,9 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
   const int r = 32 * wave + n;
   const int m = mt * kTileM + r;
   const bool row_valid = m < rows_valid;
-  const int fold = row_valid ? m / p.H : 0;
+  int h_div = p.H;
+  asm volatile("" : "+s"(h_div));  // (the division's reciprocal is then not hoisted above the segment loop)
+  const int fold = row_valid ? m / h_div : 0;
   const int t_tok = gF + fold;
   const int n_row = row_valid ? min(max(L - qlen_b + t_tok + 1, 0), L) : 0;
   const int lim = min(n_row, k1);  // keys [max(k0, lo), lim) are visible to this row
@@ -625,9 +662,10 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
       const int row = (int)(g >> 16);
       const uint32_t off = g & 0xffffu;
       const uint32_t m0 = __builtin_amdgcn_readfirstlane(d_m0 + d_step * (uint32_t)(wave + 4 * kk));
-      // fp8 tiles are loaded whole and their rows past the segment's last key
-      // are zeroed in LDS afterwards (zero_tail); bf16 tiles re-read row 0 there.
-      constexpr bool kClampRows = DT != kFp8;
+      // Tiles of pages at least a tile long (and every fp8 tile) are loaded whole and
+      // their rows past the segment's last key are zeroed in LDS afterwards (zero_tail);
+      // 16-bit tiles over shorter pages re-read row 0 there (the next page may not exist).
+      constexpr bool kClampRows = DT != kFp8 && !FAST;
       if constexpr (FAST) {
         // page_size >= TILE: the tile is TILE consecutive rows of one page
         const uint32_t voff = (!kClampRows || row < d_nvalid) ? off : off - (uint32_t)(row * RB);
@@ -654,12 +692,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
 
     // smallest visible limit and largest window start over the wave's rows:
     // tiles inside [lo_max, lim_min) need no mask
-    int lim_min = lim, lo_max = lo;
-#pragma unroll
-    for (int o2 = 32; o2 > 0; o2 >>= 1) {
-      lim_min = min(lim_min, __shfl_xor(lim_min, o2, 64));
-      lo_max = max(lo_max, __shfl_xor(lo_max, o2, 64));
-    }
+    const int lim_min = wave_min_i32(lim), lo_max = wave_max_i32(lo);
     auto tile_needs_mask = [&](int key0) { return key0 + TILE > lim_min || key0 < lo_max; };
 
     // per-lane LDS read geometry
@@ -1111,6 +1144,21 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         constexpr int CT = 32;               // keys per score block
         constexpr int HALVES = TILE / CT;    // score blocks per LDS tile
         constexpr int CDT = DT == kMixed ? kBf16 : DT;  // MFMA operand type
+        // Over pages of at least a tile the segment's last tile is loaded whole: rows past its last
+        // key hold whatever follows in the page (possibly NaN).  Their P is zero, but 0 * NaN would
+        // still reach O through the PV MFMA, so they are zeroed once the tile has landed.
+        auto zero_tail16 = [&](int t) {
+          if constexpr (FAST) {
+            const int nvalid = k1 - (k0 + t * TILE);
+            if (nvalid < TILE) {
+              lds_t* z = smem + (t % kStages) * kStageBytes + nvalid * RB;
+              const int nchunks = (TILE - nvalid) * (RB / 16);
+              for (int i = 64 * wave + lane_id_here(); i < nchunks; i += kThreads)
+                *(lds_v4i*)(z + 16 * i) = v4i{0, 0, 0, 0};
+              lds_barrier();
+            }
+          }
+        };
         issue_tile(0);
         if (1 < ntiles) issue_tile(1);
         // raw operands: bf16 / fp16 are MFMA-ready (v4i), E4M3 is widened first (v2i)
@@ -1182,7 +1230,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
             for (int r = 0; r < 16; ++r) mx_raw = fmaxf(mx_raw, sc[r]);
           } else if (i == 1) {
             const float mx = mx_raw * p.s_scale_log2;
-            const float rm = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float rm = xor32_max(mx);
             m_seen = fmaxf(m_seen, rm);
             if (m_ref == -INFINITY) m_ref = rm;
             ovf = ovf || (rm > m_ref + kTauOf<DT>);
@@ -1271,6 +1319,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         // softmax of v in its first MFMA slots.  The barrier before the publication
         // keeps it from overwriting P(v-2) while a wave still reads it.
         wait_tile_barrier(min(1, ntiles - 1));
+        if (ntiles == 1) zero_tail16(0);
         if (2 < ntiles) issue_tile(2);
         v4i pp0 = v4i{0, 0, 0, 0}, pp1 = v4i{0, 0, 0, 0};
         if (wave_active) {
@@ -1285,6 +1334,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           if (v % HALVES == 0) {
             const int tt = v / HALVES;
             wait_tile_barrier(min(1, ntiles - 1 - tt));
+            if (tt == ntiles - 1) zero_tail16(tt);
             if (tt + 2 < ntiles) issue_tile(tt + 2);
           } else {
             lds_barrier();
@@ -1341,6 +1391,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         const int nblocks = (k1 - k0 + CT - 1) / CT;
 
         wait_tile_barrier(min(1, ntiles - 1));
+        if (ntiles == 1) zero_tail16(0);
         if (2 < ntiles) issue_tile(2);
         v4i pp0 = v4i{0, 0, 0, 0}, pp1 = v4i{0, 0, 0, 0};
         if (wave_active) {
@@ -1355,6 +1406,7 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           if (v % HALVES == 0) {
             const int tt = v / HALVES;
             wait_tile_barrier(min(1, ntiles - 1 - tt));
+            if (tt == ntiles - 1) zero_tail16(tt);
             if (tt + 2 < ntiles) issue_tile(tt + 2);
           }
           if (!wave_active) continue;
@@ -2193,8 +2245,11 @@ __device__ __forceinline__ void run_segment_roles(const PartialParams& p, lds_t*
 // calls seg(sg, g, mt) for each (slice, sequence) segment in order.  Uniform
 // across the workgroup (every wave computes the same answer).
 // KEEP: lanes keep the sequences' values across the segments (kernels with registers to spare).
-template <int UK, bool WIN, bool KEEP, typename SegFn>
-__device__ __forceinline__ void for_each_segment(const PartialParams& p, int tid, int lane, SegFn&& seg) {
+// OPQ: divisors and stored values of the segment loop are made opaque inside it, so that the
+// compiler computes their vector copies there instead of keeping them across the loop (the
+// four-wave kernels, whose registers are full; the twelve-wave kernel keeps them).
+template <int UK, bool WIN, bool KEEP, bool OPQ, typename SegFn>
+__device__ __forceinline__ void for_each_segment(const PartialParams& p, int wave, int lane, SegFn&& seg) {
   int w, u;
   if (p.xcd_map) {
     // slices are dealt to the 8 XCDs in turn.  Few rows: the U workgroups of one
@@ -2268,7 +2323,7 @@ __device__ __forceinline__ void for_each_segment(const PartialParams& p, int tid
   const long long incl = wave_incl_scan_ll(own);
   const long long C = readlane_ll(incl, 63);
   int32_t* meta_u = p.meta != nullptr ? p.meta + 2 * (size_t)u * p.B : nullptr;
-  if (w == 0 && tid == 0 && meta_u != nullptr) ((long long*)(p.meta + 2 * (size_t)p.U * p.B))[u] = C;
+  if (w == 0 && wave == 0 && lane == 0 && meta_u != nullptr) ((long long*)(p.meta + 2 * (size_t)p.U * p.B))[u] = C;
   const long long a = slice_start(w, C, p.G), e = slice_start(w + 1, C, p.G);
   const long long excl = incl - own;
   // every sequence costs at least one unit, so a < C lies in exactly one non-empty lane range
@@ -2295,8 +2350,10 @@ __device__ __forceinline__ void for_each_segment(const PartialParams& p, int tid
     const long long first = S, last = first + (long long)cu * (nb - 1);
     if (first >= e) break;
     if (last >= a) {
-      const int u0 = a <= first ? 0 : (int)((a - first + cu - 1) / cu);
-      const int u1 = max(u0, min(nb, (int)((e - first + cu - 1) / cu)));
+      long long cuq = cu, Cq = C;
+      if constexpr (OPQ) asm volatile("" : "+s"(cuq), "+s"(Cq));  // (no division reciprocal is hoisted out of this loop)
+      const int u0 = a <= first ? 0 : (int)((a - first + cuq - 1) / cuq);
+      const int u1 = max(u0, min(nb, (int)((e - first + cuq - 1) / cuq)));
       SegmentCtx sg;
       sg.b = b;
       sg.u0 = u0;
@@ -2306,9 +2363,11 @@ __device__ __forceinline__ void for_each_segment(const PartialParams& p, int tid
       sg.L = v.L;
       sg.qlen = v.qlen;
       sg.tok0 = v.tok0;
-      if (meta_u != nullptr && u0 == 0 && tid == 0) {
-        meta_u[2 * b] = w;
-        meta_u[2 * b + 1] = slice_of_unit(last, C, p.G);
+      if (meta_u != nullptr && u0 == 0 && wave == 0 && lane_id_here() == 0) {
+        int wv = w;
+        if constexpr (OPQ) asm volatile("" : "+s"(wv));  // (a vector copy of w made above the loop would stay live, and spill)
+        meta_u[2 * b] = wv;
+        meta_u[2 * b + 1] = slice_of_unit(last, Cq, p.G);
       }
       seg(sg, g, mt);
     }
@@ -2328,16 +2387,21 @@ mla_split_kv_partial(PartialParams p) {
   // (only the default E4M3 instantiation: the others have no register to keep them in, and in the
   // 16-bit kernels the values held across their segments cost more than the loads they save)
   constexpr bool kKeep = DT == kFp8 && FAST && !WIN;
-  for_each_segment<Traits<DT>::kTile, WIN, kKeep>(p, tid, lane, [&](const SegmentCtx& sg, int g, int mt) {
+  // Fetch the parameters the slice walk needs together with those of the block mapping: the
+  // compiler would otherwise load them only after the mapping's early exits, a second kernel-
+  // argument round trip before the sequence lengths can be requested.
+  asm volatile("" ::"s"(p.seq_lens), "s"(p.meta), "s"(p.B), "s"(p.q_len), "s"(p.F), "s"(p.q_len_eff),
+               "s"(p.lo_cost), "s"(p.cu_q));
+  for_each_segment<Traits<DT>::kTile, WIN, kKeep, true>(p, wave, lane, [&](const SegmentCtx& sg, int g, int mt) {
     if constexpr (DT == kFp8 && FAST && !WIN) {
       // two copies of the segment code, so that the second P term costs the long sequences nothing
       if (sg.L <= kLoKeys) {
-        run_segment<DT, FAST, WIN, XPV, true>(p, smem, s_flag, sg, g, mt, wave, lane);
+        run_segment<DT, FAST, WIN, XPV, true>(p, smem, s_flag, sg, g, mt, wave, lane_id_here());
       } else {
-        run_segment<DT, FAST, WIN, XPV, false>(p, smem, s_flag, sg, g, mt, wave, lane);
+        run_segment<DT, FAST, WIN, XPV, false>(p, smem, s_flag, sg, g, mt, wave, lane_id_here());
       }
     } else {
-      run_segment<DT, FAST, WIN, XPV>(p, smem, s_flag, sg, g, mt, wave, lane);
+      run_segment<DT, FAST, WIN, XPV>(p, smem, s_flag, sg, g, mt, wave, lane_id_here());
     }
   });
 }
@@ -2351,11 +2415,11 @@ mla_split_kv_fp8_roles(PartialParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // two instantiations in separate branches: a wave's registers hold only its role's state
   if (wave < 4) {
-    for_each_segment<64, WIN, false>(p, tid, lane, [&](const SegmentCtx& sg, int g, int mt) {
+    for_each_segment<64, WIN, false, false>(p, wave, lane, [&](const SegmentCtx& sg, int g, int mt) {
       run_segment_roles<FAST, WIN, true>(p, smem, sg, g, mt, wave, lane);
     });
   } else {
-    for_each_segment<64, WIN, false>(p, tid, lane, [&](const SegmentCtx& sg, int g, int mt) {
+    for_each_segment<64, WIN, false, false>(p, wave, lane, [&](const SegmentCtx& sg, int g, int mt) {
       run_segment_roles<FAST, WIN, false>(p, smem, sg, g, mt, wave, lane);
     });
   }
@@ -2580,11 +2644,16 @@ __global__ void __launch_bounds__(256) mla_combine_wide(CombineParams p) {
 // ---------------------------------------------------------------------------
 // Merge, one wave per output row (four rows per workgroup, no barriers): for
 // batches whose sequences span few slices, where a whole workgroup per row
-// would mostly wait.  Lane l owns latent dims [8l, 8l+8); slice weights are
-// computed by the lane of the slice and broadcast with readlane; four slices'
-// partial rows are in flight at a time.
+// would mostly wait.  Lane l owns latent dims [8l, 8l+8).  The row's first
+// chunk of partial rows (16 slices of bf16, 8 of fp32) is requested together
+// with the slice LSEs, before any of the LSE arithmetic, so a row that spans at
+// most one chunk costs two memory round trips (the slice range, then LSEs and
+// partials together).  Slice weights are computed by the lane of the slice and
+// broadcast with readlane.
 // ---------------------------------------------------------------------------
+template <bool BF16P, int K>
 __global__ void __launch_bounds__(256) mla_combine_rows(CombineParams p) {
+  // K slices per chunk: K x 16 bytes of bf16 partials per lane, or K x 32 bytes of fp32
   const int lane = threadIdx.x & 63;
   // wave-uniform: the row, its slice range and T are then scalar values
   const long long grow = (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -2599,68 +2668,74 @@ __global__ void __launch_bounds__(256) mla_combine_rows(CombineParams p) {
   const int n = w1 - w0 + 1;
   // (a slice without units of the sequence ran an empty segment: LSE -inf, O = 0)
   auto lse_of = [&](int s) -> float { return p.part_lse[(size_t)(s + b) * p.rows_per_b + row]; };
-  float mx = -INFINITY;
-  for (int i = lane; i < n; i += 64) mx = fmaxf(mx, lse_of(w0 + i));
+  const size_t st_bytes = (size_t)p.rows_per_b * kDv * (BF16P ? 2 : 4);  // bytes between consecutive slots
+  const uint8_t* src0 =
+      (const uint8_t*)p.part_o + ((size_t)(w0 + b) * p.rows_per_b + row) * kDv * (BF16P ? 2 : 4) +
+      (BF16P ? 16 : 32) * lane;
+  // requests: the LSEs of the first 64 slices (one per lane) and the first chunk's partial rows
+  const float l0 = lane < n ? lse_of(w0 + lane) : -INFINITY;
+  using V = std::conditional_t<BF16P, v4i, v4f>;
+  V x[K], y[K];  // y: the second 16 bytes of fp32 partials
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    x[j] = V{0, 0, 0, 0};
+    y[j] = V{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    if (j < n) {
+      const V* a = (const V*)(src0 + (size_t)j * st_bytes);
+      x[j] = a[0];
+      if constexpr (!BF16P) y[j] = a[1];
+    }
+  }
+  float mx = l0;
+  for (int i = lane + 64; i < n; i += 64) mx = fmaxf(mx, lse_of(w0 + i));
   mx = wave_max(mx);
   float sum = 0.f;
-  if (mx > -INFINITY)
-    for (int i = lane; i < n; i += 64) sum += expf(lse_of(w0 + i) - mx);
+  if (mx > -INFINITY) {
+    sum = expf(l0 - mx);  // 0 on lanes past n
+    for (int i = lane + 64; i < n; i += 64) sum += expf(lse_of(w0 + i) - mx);
+  }
   sum = wave_sum(sum);
   const float lse_out = mx > -INFINITY ? mx + logf(sum) : -INFINITY;
 
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  const size_t st_rows = (size_t)p.rows_per_b * kDv;  // elements between consecutive slots
-  const size_t base = ((size_t)(w0 + b) * p.rows_per_b + row) * kDv + 8 * lane;
-  // slots of empty slices hold stale bytes: select, never multiply them by 0
-  auto add_bf16 = [&](const v4i& x, float wgt) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t u = (uint32_t)x[e];
-      acc[2 * e] += wgt > 0.f ? wgt * __builtin_bit_cast(float, u << 16) : 0.f;
-      acc[2 * e + 1] += wgt > 0.f ? wgt * __builtin_bit_cast(float, u & 0xffff0000u) : 0.f;
-    }
-  };
-  auto add_f32 = [&](const v4f& x0, const v4f& x1, float wgt) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] += wgt > 0.f ? wgt * x0[e] : 0.f;
-      acc[4 + e] += wgt > 0.f ? wgt * x1[e] : 0.f;
-    }
-  };
   if (mx > -INFINITY) {
     for (int c0 = 0; c0 < n; c0 += 64) {
       const int cn = min(64, n - c0);
-      const float wl = lane < cn ? expf(lse_of(w0 + c0 + lane) - lse_out) : 0.f;
-      auto wgt_of = [&](int i) -> float {
-        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), i));
-      };
-      int i = 0;
-      if (p.part_bf16) {
-        const uint16_t* src = (const uint16_t*)p.part_o + base + (size_t)c0 * st_rows;
-        for (; i + 4 <= cn; i += 4) {
-          v4i x[4];
+      const float wl = lane < cn ? expf((c0 == 0 ? l0 : lse_of(w0 + c0 + lane)) - lse_out) : 0.f;
+      for (int i = 0; i < cn; i += K) {
+        if (c0 + i > 0) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) x[j] = *(const v4i*)(src + (size_t)(i + j) * st_rows);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) add_bf16(x[j], wgt_of(i + j));
-        }
-        for (; i < cn; ++i) add_bf16(*(const v4i*)(src + (size_t)i * st_rows), wgt_of(i));
-      } else {
-        const float* src = (const float*)p.part_o + base + (size_t)c0 * st_rows;
-        for (; i + 4 <= cn; i += 4) {
-          v4f x0[4], x1[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            x0[j] = *(const v4f*)(src + (size_t)(i + j) * st_rows);
-            x1[j] = *(const v4f*)(src + (size_t)(i + j) * st_rows + 4);
+          for (int j = 0; j < K; ++j) {
+            if (i + j < cn) {
+              const V* a = (const V*)(src0 + (size_t)(c0 + i + j) * st_bytes);
+              x[j] = a[0];
+              if constexpr (!BF16P) y[j] = a[1];
+            }
           }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) add_f32(x0[j], x1[j], wgt_of(i + j));
         }
-        for (; i < cn; ++i)
-          add_f32(*(const v4f*)(src + (size_t)i * st_rows), *(const v4f*)(src + (size_t)i * st_rows + 4), wgt_of(i));
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          // slots of empty slices hold stale bytes: select, never multiply them by 0
+          const float wgt =
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), min(i + j, 63)));
+          const bool use = i + j < cn && wgt > 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (BF16P) {
+              const uint32_t u = (uint32_t)x[j][e];
+              acc[2 * e] += use ? wgt * __builtin_bit_cast(float, u << 16) : 0.f;
+              acc[2 * e + 1] += use ? wgt * __builtin_bit_cast(float, u & 0xffff0000u) : 0.f;
+            } else {
+              acc[e] += use ? wgt * x[j][e] : 0.f;
+              acc[4 + e] += use ? wgt * y[j][e] : 0.f;
+            }
+          }
+        }
       }
     }
   }
@@ -2775,9 +2850,15 @@ hipError_t launch_partial(const PartialParams& p_in, int dtype, bool fast_pages,
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
   const long long rows = (long long)p.B * p.rows_per_b;
-  if (combine_per_wave(p.B, p.G)) {
+  if (p.merge_kernel == 2 || combine_per_wave(p.B, p.G)) {
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-    hipLaunchKernelGGL(mla_combine_rows, grid, block, 0, stream, p);
+    // chunk size: about a row's slices (G / B + 1 on average), fewer registers for fewer slices
+    const long long G = p.G, B = p.B;
+    if (p.part_bf16 && G >= 7 * B) hipLaunchKernelGGL((mla_combine_rows<true, 16>), grid, block, 0, stream, p);
+    else if (p.part_bf16 && G >= 2 * B) hipLaunchKernelGGL((mla_combine_rows<true, 8>), grid, block, 0, stream, p);
+    else if (p.part_bf16) hipLaunchKernelGGL((mla_combine_rows<true, 4>), grid, block, 0, stream, p);
+    else if (G >= 2 * B) hipLaunchKernelGGL((mla_combine_rows<false, 8>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((mla_combine_rows<false, 4>), grid, block, 0, stream, p);
   } else if (p.merge_kernel == 1) {
     const dim3 grid((unsigned)rows), block(256);
     hipLaunchKernelGGL(mla_combine, grid, block, 0, stream, p);

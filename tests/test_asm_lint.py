@@ -67,3 +67,48 @@ def test_spill_in_a_loop_without_mfmas_is_allowed():
 def test_spill_outside_loops_is_allowed():
     body = "\tscratch_store_dword off, v3, off\n.LBB2_1:  ; =>This Loop Header: Depth=1\n\tv_add_u32_e32 v1, v2, v3\n"
     assert _lint(body) == []
+
+
+def _build_module():
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from mla_paged_kv_decode_amd import build
+    return build
+
+
+def test_spill_gate_covers_the_default_instantiations():
+    b = _build_module()
+    pre = "_ZN3mla12_GLOBAL__N_120mla_split_kv_partialI"
+    gated = [pre + "Li2ELb1ELb0ELb1EEEvNS_13PartialParamsE",   # E4M3, pages >= a tile, no window
+             pre + "Li1ELb1ELb0ELb0EEEvNS_13PartialParamsE",   # bf16, own rows
+             pre + "Li1ELb1ELb1ELb1EEEvNS_13PartialParamsE",   # bf16, cross-wave, window
+             pre + "Li3ELb1ELb0ELb1EEEvNS_13PartialParamsE",   # fp16
+             pre + "Li4ELb1ELb0ELb0EEEvNS_13PartialParamsE",   # bf16 q over E4M3
+             "_ZN3mla12_GLOBAL__N_116mla_combine_wideILb1EEEvNS_13CombineParamsE",
+             "_ZN3mla12_GLOBAL__N_115mla_kv_pack_fp8ENS_10PackParamsE"]
+    free = [pre + "Li2ELb1ELb1ELb1EEEvNS_13PartialParamsE",     # E4M3 four-wave kernel with a window
+            pre + "Li2ELb0ELb0ELb1EEEvNS_13PartialParamsE",     # E4M3 over short pages
+            pre + "Li1ELb0ELb0ELb0EEEvNS_13PartialParamsE",     # bf16 over short pages
+            "_ZN3mla12_GLOBAL__N_122mla_split_kv_fp8_rolesILb1ELb0EEEvNS_13PartialParamsE"]
+    assert all(b.must_not_spill(k) for k in gated)
+    assert not any(b.must_not_spill(k) for k in free)
+    res = {k: {"VGPRs Spill": 0} for k in gated + free}
+    assert b.spill_gate(res) == []
+    res[gated[0]]["VGPRs Spill"] = 3
+    res[free[0]]["VGPRs Spill"] = 15
+    bad = b.spill_gate(res)
+    assert len(bad) == 1 and gated[0] in bad[0]
+
+
+def test_built_library_has_no_spills_in_the_gated_kernels():
+    b = _build_module()
+    path = os.path.join(os.path.dirname(b.LIB), "kernel_resources.txt")
+    if not os.path.exists(path):
+        import pytest
+        pytest.skip("library not built here (kernel_resources.txt is written by the build)")
+    rows = {}
+    for line in open(path):
+        name, _, rest = line.partition(": ")
+        fields = dict(kv.split("=") for kv in rest.split())
+        rows[name] = {"VGPRs Spill": int(fields["vgpr_spill"])}
+    assert any(b.must_not_spill(k) for k in rows)
+    assert b.spill_gate(rows) == []

@@ -148,7 +148,7 @@ def test_options_layout_matches_header():
 def test_kernel_and_merge_options_validated_before_any_device_work():
     L = mla.lib()
     shape = _shape()
-    for kw, word in ((dict(kernel=3), b"kernel"), (dict(kernel=-1), b"kernel"), (dict(merge=2), b"merge")):
+    for kw, word in ((dict(kernel=3), b"kernel"), (dict(kernel=-1), b"kernel"), (dict(merge=3), b"merge"), (dict(merge=-1), b"merge")):
         opts = mla.options(**kw)
         rc = L.mla_decode_ex(ctypes.byref(shape), 16, 16, 16, 16, 1.0, 1.0, 1.0, 16, 16, None, 0, None,
                              ctypes.byref(opts))

@@ -83,18 +83,20 @@ def test_four_wave_fp8_kernel_forced_splits(dtype, splits):
 @pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
 @pytest.mark.parametrize("partial_fp32", [False, True])
 def test_both_merge_kernels(dtype, partial_fp32):
-    """The wide merge (default) and the workgroup-per-row merge, on rows spread over many slices
-    (ragged, with empty slices): both within the bars, and the same up to summation order."""
+    """The wide merge (default), the workgroup-per-row merge and the per-wave merge, on rows spread
+    over many slices (ragged, with empty slices; more than a chunk of the per-wave merge): all within
+    the bars, and the same up to summation order."""
     x = mi.make_inputs(2, 2, 64, dtype, ("list", [9000, 37]), seed=77)
     print(f"merge dtype={dtype} partial_fp32={partial_fp32}", flush=True)
     ref = run_oracle(x)
     res = []
-    for merge in (0, 1):
+    for merge in (0, 1, 2):
         out, lse = run_gpu(x, opts=mla.options(num_splits=150, partial_fp32=partial_fp32, merge=merge))
         assert_parity(x, out, lse, ref, partial_fp32=partial_fp32 or dtype != mi.FP8_E4M3)
         res.append((out.float(), lse))
-    assert float((res[0][0] - res[1][0]).abs().max()) <= 2.0 ** -7
-    assert float((res[0][1] - res[1][1]).abs().max()) <= 1e-5
+    for k in (1, 2):
+        assert float((res[0][0] - res[k][0]).abs().max()) <= 2.0 ** -7
+        assert float((res[0][1] - res[k][1]).abs().max()) <= 1e-5
 
 
 @pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3, mi.BF16_Q_E4M3_KV])
