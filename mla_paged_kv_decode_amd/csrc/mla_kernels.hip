@@ -2564,39 +2564,49 @@ __global__ void __launch_bounds__(256) mla_combine_wide(CombineParams p) {
   const int n = w1 - w0 + 1;
   // (a slice without units of the sequence ran an empty segment: LSE -inf, O = 0)
   auto lse_of = [&](int s) -> float { return p.part_lse[(size_t)(s + b) * p.rows_per_b + row]; };
-  float mx = -INFINITY;
-  for (int i = lane; i < n; i += 64) mx = fmaxf(mx, lse_of(w0 + i));
+  const int grp = lane / LPS, sub = lane - grp * LPS;  // this lane: slice grp of each SPI, 16 bytes sub
+  const size_t slot_elems = (size_t)p.rows_per_b * kDv;  // elements between consecutive slots
+  const size_t base = ((size_t)(w0 + b) * p.rows_per_b + row) * kDv + 128 * quarter + (BF16P ? 8 : 4) * sub;
+  auto load_chunk = [&](int c0, int cn, v4i* x) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int sl = SPI * i + grp;  // slice of the chunk this lane loads with instruction i
+      if (sl < cn) {
+        if constexpr (BF16P) {
+          x[i] = *(const v4i*)((const uint16_t*)p.part_o + base + (size_t)(c0 + sl) * slot_elems);
+        } else {
+          x[i] = *(const v4i*)((const float*)p.part_o + base + (size_t)(c0 + sl) * slot_elems);
+        }
+      }
+    }
+  };
+  // requests: the LSEs of the first 64 slices (one per lane) and the first chunk's partials,
+  // before any of the LSE arithmetic
+  const float l0 = lane < n ? lse_of(w0 + lane) : -INFINITY;
+  v4i x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = v4i{0, 0, 0, 0};
+  load_chunk(0, min(CS, n), x);
+  float mx = l0;
+  for (int i = lane + 64; i < n; i += 64) mx = fmaxf(mx, lse_of(w0 + i));
   mx = wave_max(mx);
   float sum = 0.f;
-  if (mx > -INFINITY)
-    for (int i = lane; i < n; i += 64) sum += expf(lse_of(w0 + i) - mx);
+  if (mx > -INFINITY) {
+    sum = expf(l0 - mx);  // 0 on lanes past n
+    for (int i = lane + 64; i < n; i += 64) sum += expf(lse_of(w0 + i) - mx);
+  }
   sum = wave_sum(sum);
   const float lse_out = mx > -INFINITY ? mx + logf(sum) : -INFINITY;
 
-  const int grp = lane / LPS, sub = lane - grp * LPS;  // this lane: slice grp of each SPI, 16 bytes sub
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  const size_t slot_elems = (size_t)p.rows_per_b * kDv;  // elements between consecutive slots
-  const size_t base = ((size_t)(w0 + b) * p.rows_per_b + row) * kDv + 128 * quarter + (BF16P ? 8 : 4) * sub;
   if (mx > -INFINITY) {
     for (int c0 = 0; c0 < n; c0 += CS) {
       const int cn = min(CS, n - c0);
       // slice weights of the chunk, one per lane (lanes past the chunk: 0)
-      const float wl = lane < cn ? expf(lse_of(w0 + c0 + lane) - lse_out) : 0.f;
-      v4i x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int sl = SPI * i + grp;  // slice of the chunk this lane loads with instruction i
-        x[i] = v4i{0, 0, 0, 0};
-        if (sl < cn) {
-          if constexpr (BF16P) {
-            x[i] = *(const v4i*)((const uint16_t*)p.part_o + base + (size_t)(c0 + sl) * slot_elems);
-          } else {
-            x[i] = *(const v4i*)((const float*)p.part_o + base + (size_t)(c0 + sl) * slot_elems);
-          }
-        }
-      }
+      const float wl = lane < cn ? expf((c0 == 0 ? l0 : lse_of(w0 + c0 + lane)) - lse_out) : 0.f;
+      if (c0 > 0) load_chunk(c0, cn, x);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int sl = SPI * i + grp;
@@ -2620,12 +2630,14 @@ __global__ void __launch_bounds__(256) mla_combine_wide(CombineParams p) {
       }
     }
   }
-  // lanes sub, sub + LPS, ... hold the same dims: sum across the lane groups
+  // lanes sub, sub + LPS, ... hold the same dims: sum across the lane groups (lane ^ 16 by
+  // ds_swizzle inside each half, lane ^ 32 by v_permlane32_swap)
 #pragma unroll
-  for (int o2 = LPS; o2 < 64; o2 <<= 1) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (BF16P || e < 4) acc[e] += __shfl_xor(acc[e], o2, 64);
+  for (int e = 0; e < 8; ++e) {
+    if (BF16P || e < 4) {
+      if constexpr (LPS == 16)
+        acc[e] += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, acc[e]), (16 << 10) | 31));
+      acc[e] = xor32_sum(acc[e]);
     }
   }
   if (lane < LPS) {
