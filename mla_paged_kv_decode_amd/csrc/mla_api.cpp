@@ -275,11 +275,12 @@ int decode_impl(const mla_shape* s, const void* q, const void* kv, const int32_t
   p.num_pages = s->num_pages;
   p.s_scale_log2 = (float)((double)softmax_scale * (double)q_scale * (double)kv_scale * 1.4426950408889634074);
   p.v_scale = kv_scale;
-  // Partial outputs: bf16 for E4M3 caches (their bar is 5e-2, and the partials' round trip is
-  // the step's largest overhead), fp32 for 16-bit caches (a bf16 rounding of every slice before
-  // the merge would eat most of their 1e-2 bar on rows merged from many slices).
-  const bool e4m3_kv = dt == mla::kFp8 || dt == mla::kMixed;
-  p.part_bf16 = (!(opt && opt->partial_fp32) && e4m3_kv) ? 1 : 0;
+  // Partial outputs: bf16 for E4M3 and bf16 caches (the partials' round trip is the step's largest
+  // overhead after the KV stream; rounding each slice's O to bf16 moves the merged row by at most
+  // 2^-9 of sum_j w_j |v_j|), fp32 for fp16 caches (their V values are not bf16 values: a single
+  // key's V must come back as stored).
+  const bool bf16_part = dt == mla::kFp8 || dt == mla::kMixed || dt == mla::kBf16;
+  p.part_bf16 = (!(opt && opt->partial_fp32) && bf16_part) ? 1 : 0;
   p.window = opt ? opt->window : 0;
   p.cu_q = cu_q;
   p.total_q = total_q;

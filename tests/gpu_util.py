@@ -37,6 +37,8 @@ def half_ulp_bf16(x):
 P_ROUND = {mi.BF16: 2.0 ** -8, mi.FP8_E4M3: 2.0 ** -4, mi.FP16: 2.0 ** -11, mi.BF16_Q_E4M3_KV: 2.0 ** -8}
 U_OUT = 2.0 ** -8
 SLACK = 2e-4
+# dtypes whose split partials are bf16 (fp16 caches keep fp32 partials)
+BF16_PARTIALS = (mi.FP8_E4M3, mi.BF16_Q_E4M3_KV, mi.BF16)
 
 
 def o_tol(dtype):
@@ -100,8 +102,8 @@ def assert_parity(x, out, lse, ref, rows=None, partial_fp32=False, per_seq=False
     u = P_ROUND[x.dtype]
     pre = u / (1.0 - u) * (absv + np.abs(O_ref))
     bound = pre + U_OUT * (np.abs(O_ref) + pre) + SLACK
-    if not partial_fp32 and mi.kv_format(x.dtype) == mi.FP8_E4M3:
-        bound += U_OUT * absv  # split partials of E4M3 caches are rounded to bf16 before the merge
+    if not partial_fp32 and x.dtype in BF16_PARTIALS:
+        bound += U_OUT * absv  # split partials of E4M3 and bf16 caches are rounded to bf16 before the merge
     o_err = float(err.max()) if err.size else 0.0
     fin = ~empty
     l_err = float(np.max(np.abs(L[fin] - lse_ref[fin]))) if fin.any() else 0.0

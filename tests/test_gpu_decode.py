@@ -92,7 +92,7 @@ def test_both_merge_kernels(dtype, partial_fp32):
     res = []
     for merge in (0, 1, 2):
         out, lse = run_gpu(x, opts=mla.options(num_splits=150, partial_fp32=partial_fp32, merge=merge))
-        assert_parity(x, out, lse, ref, partial_fp32=partial_fp32 or dtype != mi.FP8_E4M3)
+        assert_parity(x, out, lse, ref, partial_fp32=partial_fp32)
         res.append((out.float(), lse))
     for k in (1, 2):
         assert float((res[0][0] - res[k][0]).abs().max()) <= 2.0 ** -7
