@@ -99,6 +99,26 @@ def test_both_merge_kernels(dtype, partial_fp32):
         assert float((res[0][1] - res[k][1]).abs().max()) <= 1e-5
 
 
+# The per-wave merge takes its rows' slices in chunks sized by the average slices per row
+# (bf16 partials: 16 when G >= 7B, 8 when G >= 2B, else 4; fp32: 8 or 4); a long sequence among
+# short ones spans more slices than a chunk, so its rows take several chunks.
+PER_WAVE_MERGE_CASES = [
+    (2, 24, [3000, 2500]),                                        # 16 (fp32: 8)
+    (4, 16, [5000, 300, 900, 1200]),                              # 8
+    (8, 8, [6000, 100, 200, 50, 300, 10, 400, 20]),              # 4
+]
+
+
+@pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3])
+@pytest.mark.parametrize("partial_fp32", [False, True])
+@pytest.mark.parametrize("B,splits,lens", PER_WAVE_MERGE_CASES)
+def test_per_wave_merge_chunks(dtype, partial_fp32, B, splits, lens):
+    x = mi.make_inputs(B, 1, 16, dtype, ("list", lens), seed=900 + B + splits)
+    print(f"per-wave merge dtype={dtype} partial_fp32={partial_fp32} B={B} splits={splits} lens={lens}", flush=True)
+    out, lse = run_gpu(x, opts=mla.options(num_splits=splits, partial_fp32=partial_fp32))
+    assert_parity(x, out, lse, run_oracle(x), partial_fp32=partial_fp32)
+
+
 @pytest.mark.parametrize("dtype", [mi.BF16, mi.FP8_E4M3, mi.BF16_Q_E4M3_KV])
 def test_fold_and_partial_precision_options(dtype):
     x = mi.make_inputs(2, 4, 16, dtype, ("list", [1800, 650]), seed=41)
