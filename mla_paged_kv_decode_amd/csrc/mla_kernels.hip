@@ -530,7 +530,10 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
     const int keep = row_valid ? -1 : 0;
 #pragma unroll
     for (int c = 0; c < QSTEPS; ++c) {
-      const v4i x = *(const v4i*)(qrow + 2 * (16 * c + 8 * hh)) & keep;
+      // (bf16 q over an E4M3 cache: step c holds dims 32(c/2) + 16hh + 8(c%2) + [0, 8), the order
+      // in which that kernel reads its K operands, 16 bytes per pair of steps)
+      const int d0 = DT == kMixed ? 32 * (c >> 1) + 16 * hh + 8 * (c & 1) : 16 * c + 8 * hh;
+      const v4i x = *(const v4i*)(qrow + 2 * d0) & keep;
       qreg[c] = v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0};
     }
     // Q must be in registers before the KV ring starts: the compiler cannot see the
@@ -711,11 +714,13 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
       vaddr[1] = kbase * RB + (((2 + dsub) ^ s8) * 16) + 8 * c8;
       vaddr[2] = vaddr[3] = 0;
     } else if constexpr (DT == kMixed) {
-      // K: eight E4M3 codes of key row n, dims [16c + 8hh, +8) (chunk c, half hh);
+      // K: sixteen E4M3 codes of key row n per pair j of 16-dim steps, dims [32j + 16hh, +16)
+      // (16-byte chunk 2j + hh: slot hh of its group of four for even j, 2 + hh for odd j);
       // V: the transposing 8-bit reads of the fp8 path, one read per operand
       const int sw = (n >> 2) & 3;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) kaddr[x] = n * RB + ((x ^ sw) * 16) + 8 * hh;
+      kaddr[0] = n * RB + ((hh ^ sw) * 16);
+      kaddr[1] = n * RB + (((2 + hh) ^ sw) * 16);
+      kaddr[2] = kaddr[3] = 0;
       const int grp = lane >> 4, hs = grp >> 1, dsub = grp & 1, uu = lane & 15, rr = uu >> 1, c8 = uu & 1;
       const int kbase = 8 * (rr >> 2) + 4 * hs + (rr & 3);
       const int s8 = (2 * (rr >> 2) + hs) & 3;
@@ -1163,9 +1168,10 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         if (1 < ntiles) issue_tile(1);
         // raw operands: bf16 / fp16 are MFMA-ready (v4i), E4M3 is widened first (v2i)
         using raw_t = std::conditional_t<DT == kMixed, v2i, v4i>;
-        auto kread = [&](const lds_t* st, int c) -> raw_t {
+        auto kread = [&](const lds_t* st, int c) -> v4i {
           if constexpr (DT == kMixed) {
-            return *(const lds_v2i*)(st + kaddr[c & 3] + 64 * (c >> 2));
+            // the 16 codes of step pair c (steps 2c and 2c+1)
+            return *(const lds_v4i*)(st + kaddr[c & 1] + 64 * (c >> 1));
           } else {
             return *(const lds_v4i*)(st + kaddr[c & 3] + 128 * (c >> 2));
           }
@@ -1196,17 +1202,41 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         constexpr int kAhead = 4, kVAhead = 2;
         auto qk = [&](const lds_t* st, v16f& s) {
           s = v16f{0};
-          raw_t a[kAhead];
+          if constexpr (DT == kMixed) {
+            // One 16-byte read per lane and pair of steps (two pairs ahead), its halves widened
+            // one MFMA ahead.  Over 576-byte rows, 8-byte reads of one step put rows n and
+            // n + 16 on the same banks; 16-byte reads of 16 consecutive rows cover each bank once.
+            constexpr int kP = kAhead / 2;
+            v4i a[kP];
 #pragma unroll
-          for (int c = 0; c < kAhead; ++c) a[c] = kread(st, c);
-          v4i cur = ready(a[0]);
+            for (int j = 0; j < kP; ++j) a[j] = kread(st, j);
+            v4i cur = widen_e4m3_bf16(v2i{a[0][0], a[0][1]});
 #pragma unroll
-          for (int c = 0; c < 36; ++c) {
-            const v4i qb = v4i{qreg[c][0], qreg[c][1], qreg[c][2], qreg[c][3]};
-            qk_mfma_h16<CDT>(s, cur, qb, c == 35);
-            if (c + kAhead < 36) a[c % kAhead] = kread(st, c + kAhead);
-            if (c + 1 < 36) cur = ready(a[(c + 1) % kAhead]);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int c = 0; c < 36; ++c) {
+              const v4i qb = v4i{qreg[c][0], qreg[c][1], qreg[c][2], qreg[c][3]};
+              qk_mfma_h16<CDT>(s, cur, qb, c == 35);
+              const int j = c >> 1;
+              if ((c & 1) == 0) {
+                cur = widen_e4m3_bf16(v2i{a[j % kP][2], a[j % kP][3]});
+              } else {
+                if (j + kP < 18) a[j % kP] = kread(st, j + kP);
+                if (c + 1 < 36) cur = widen_e4m3_bf16(v2i{a[(j + 1) % kP][0], a[(j + 1) % kP][1]});
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
+            raw_t a[kAhead];
+#pragma unroll
+            for (int c = 0; c < kAhead; ++c) a[c] = kread(st, c);
+            v4i cur = ready(a[0]);
+#pragma unroll
+            for (int c = 0; c < 36; ++c) {
+              const v4i qb = v4i{qreg[c][0], qreg[c][1], qreg[c][2], qreg[c][3]};
+              qk_mfma_h16<CDT>(s, cur, qb, c == 35);
+              if (c + kAhead < 36) a[c % kAhead] = kread(st, c + kAhead);
+              if (c + 1 < 36) cur = ready(a[(c + 1) % kAhead]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
         };
         float mx_raw = -INFINITY, mref = 0.f, lsum = 0.f;
