@@ -111,8 +111,8 @@ Plan make_plan(int B, int q_len, int H, int max_seq_len, int num_cus, const mla_
     pl.bytes = 0;
     pl.off_part_o = pl.off_part_lse = pl.off_meta = 0;
   } else {
-    // partial outputs are sized for fp32 (the plan carries no dtype; E4M3 caches
-    // write bf16 partials into the first half of the region)
+    // partial outputs are sized for fp32 (the plan carries no dtype; E4M3 and bf16
+    // caches write bf16 partials into the first half of the region)
     const size_t slots = (size_t)G + (size_t)B;
     const size_t esz = 4;
     pl.off_part_o = 0;
