@@ -19,6 +19,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmla_decode.so")
 SOURCES = [os.path.join(HERE, "csrc", "mla_kernels.hip"), os.path.join(HERE, "csrc", "mla_api.cpp")]
+# The HBM -> LDS streaming probe bench.py measures the achievable read rate with: a library of its
+# own, outside the decode library's C ABI.
+PROBE_LIB = os.path.join(HERE, "libmla_stream_probe.so")
+PROBE_SOURCES = [os.path.join(HERE, "csrc", "stream_probe.hip")]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -132,7 +136,20 @@ def build(verbose: bool = False) -> str:
         f.write("\n".join(lines) + "\n")
     if verbose:
         print("\n".join(lines))
+    build_probe()
     return LIB
+
+
+def build_probe() -> str:
+    tmp = PROBE_LIB + ".tmp"
+    flags = [f for f in FLAGS if not f.startswith("-Rpass")]
+    proc = subprocess.run([_hipcc(), *flags, *PROBE_SOURCES, "-o", tmp], stdout=subprocess.PIPE,
+                          stderr=subprocess.STDOUT, text=True)
+    if proc.returncode != 0:
+        sys.stderr.write(proc.stdout)
+        raise RuntimeError(f"hipcc failed on the streaming probe ({proc.returncode})")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

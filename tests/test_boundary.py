@@ -410,3 +410,22 @@ def test_descriptor_layouts_match_header():
         assert [f[1] for f in fields] == [f[0] for f in cls._fields_], name
     assert ctypes.sizeof(mla.MlaTensor) == 8 + 4 + 4 + 32 + 32
     assert ctypes.sizeof(mla.MlaWorkspace) == 8 + 8 + 4 + 4
+
+
+def test_stream_probe_library_exports_its_entry_point():
+    """The HBM -> LDS streaming probe bench.py measures the achievable read rate with is built beside the
+    library and exports its one C entry point; its argument checks run without a GPU."""
+    import ctypes
+    import os
+
+    from mla_paged_kv_decode_amd import build as b
+
+    if not os.path.exists(b.PROBE_LIB):
+        pytest.skip("probe library not built here")
+    L = ctypes.CDLL(b.PROBE_LIB)
+    f = L.mla_stream_probe
+    f.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(None, 1 << 20, 0, None) == -1          # no buffer
+    assert f(16, 36864 - 1, 0, None) == -1          # less than one tile
+    assert f(16, 1 << 20, -1, None) == -1           # negative workgroup count

@@ -741,3 +741,20 @@ def test_ragged_window_and_more_tokens_than_keys():
                                  max_seq_len=x.max_seq_len, opts=mla.options(window=50, num_splits=9))
     torch.cuda.synchronize()
     assert_parity(x, out, lse, ref)
+
+
+def test_stream_probe_runs():
+    """The HBM -> LDS streaming probe bench.py reports the achievable read rate with: one pass over
+    a 64 MiB buffer (a partial last round of tiles included) completes."""
+    import ctypes
+
+    from mla_paged_kv_decode_amd import build as b
+
+    L = ctypes.CDLL(b.PROBE_LIB)
+    f = L.mla_stream_probe
+    f.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    buf = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda:0")
+    print("stream probe over 64 MiB", flush=True)
+    assert f(buf.data_ptr(), buf.numel(), 0, torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
