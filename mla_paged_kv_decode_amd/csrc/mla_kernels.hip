@@ -1080,6 +1080,11 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         // Q: each wave's 32 rows (18 KiB, one contiguous block of the folded
         // query) are copied straight into ring stages 2-3, which stay free
         // until tile 2 is issued, so their latency overlaps that of tiles 0-1.
+        // Rows are laid out as the KV tiles are: 16-byte chunks XOR-swizzled
+        // by (row / 4) % 4 inside each group of four, so that the reads of one
+        // chunk column by sixteen consecutive rows meet sixteen bank groups
+        // (unswizzled, 576-byte rows put them on four).  The swizzle is made
+        // on the source side: LDS chunk p of row r takes chunk p ^ ((r/4)%4).
         constexpr int kQDma = 32 * kDqk / 1024;  // 18 one-KiB loads per wave
         {
           const uint8_t* qblk = p.q + ((size_t)tok0 + gF) * p.H * kDqk;
@@ -1090,9 +1095,11 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
           for (int kk = 0; kk < kQDma; ++kk) {
             const int o = 1024 * kk + 16 * qlane;
             const int qn = o / kDqk;
+            const int pc = (o - qn * kDqk) >> 4;                  // LDS chunk of row qn
+            const int lc = (pc & ~3) | ((pc & 3) ^ ((qn >> 2) & 3));  // source chunk
             const int mrow = mt * kTileM + 32 * wave + qn;
             const int src_row = mrow < rows_valid ? mrow : 0;
-            dma16_vaddr(qblk + (size_t)src_row * kDqk + (o - qn * kDqk),
+            dma16_vaddr(qblk + (size_t)src_row * kDqk + 16 * lc,
                         __builtin_amdgcn_readfirstlane(qlds + 1024u * (uint32_t)kk));
           }
         }
@@ -1102,12 +1109,18 @@ __device__ __forceinline__ void run_segment(const PartialParams& p, lds_t* smem,
         issue_tile(1);  // a dummy tile when the segment has one tile
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kDmaPerWave) : "memory");  // this wave's Q has landed
         {
-          const lds_t* qs = smem + 2 * kStageBytes + wave * 32 * kDqk + n * kDqk + 32 * hh;
+          // logical chunks 4c + 2hh and 4c + 2hh + 1 of row n sit at the 32-byte pair
+          // 4c + ((2hh ^ sw) & 2), in swapped order when sw = (n / 4) % 4 is odd
+          const int qsw = (n >> 2) & 3;
+          const lds_t* qs = smem + 2 * kStageBytes + wave * 32 * kDqk + n * kDqk + (((2 * hh) ^ qsw) & 2) * 16;
+          const bool qswap = (qsw & 1) != 0;
           const int keep = row_valid ? -1 : 0;
 #pragma unroll
           for (int c = 0; c < QSTEPS; ++c) {
-            const v4i x0 = *(const lds_v4i*)(qs + 64 * c) & keep;
-            const v4i x1 = *(const lds_v4i*)(qs + 64 * c + 16) & keep;
+            const v4i y0 = *(const lds_v4i*)(qs + 64 * c);
+            const v4i y1 = *(const lds_v4i*)(qs + 64 * c + 16);
+            const v4i x0 = (qswap ? y1 : y0) & keep;
+            const v4i x1 = (qswap ? y0 : y1) & keep;
             qreg[c] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
           }
         }
